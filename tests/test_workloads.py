@@ -1,0 +1,68 @@
+"""Input generator and workload bookkeeping (CPU)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from workloads import gen as G
+
+
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        # exact ties: halfway between neighbouring bf16 values
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130 * 3], dtype=np.float32),
+    ])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(G.bf16_rne_bits(x), want)
+    assert G.bf16_rne_bits(np.array([1 + 2 ** -8], np.float32))[0] == 0x3F80   # tie -> even
+    assert G.bf16_rne_bits(np.array([1 + 3 * 2 ** -8], np.float32))[0] == 0x3F82
+
+
+def test_bf16_rounding_rejects_nonfinite():
+    with pytest.raises(ValueError):
+        G.bf16_rne_bits(np.array([np.inf], np.float32))
+
+
+def test_streams_are_deterministic_and_per_head():
+    a = G.bf16_heads(0, G.TAG_Q, 3, 1, [0, 1, 2], 7, 8)
+    b = G.bf16_heads(0, G.TAG_Q, 3, 1, [2], 7, 8)
+    c = G.bf16_heads(0, G.TAG_Q, 3, 1, [0, 1, 2], 7, 8)
+    assert np.array_equal(a, c)
+    assert np.array_equal(a[2], b[0])           # a head's stream is independent of the others
+    assert not np.array_equal(a[0], a[1])
+    d = G.bf16_heads(1, G.TAG_Q, 3, 1, [0], 7, 8)
+    assert not np.array_equal(a[0], d[0])
+
+
+def test_workload_key_counts():
+    want = {"tiny": 804, "v01_unit": 9372, "v02_rank_share": 61880,
+            "v02_whole_performer": 61880, "audio_long_history": 244772}
+    for w in W.ALL:
+        assert w.n_keys == want[w.name]
+    assert W.TINY.cache_len == 552 and W.V02_RANK.cache_len == 60960
+    assert W.AUDIO_LONG.cache_len == 244768
+    assert W.V02_RANK.latent_elems == 920 * 10 * 128
+
+
+def test_history_matches_unit_by_unit_construction():
+    w = W.TINY
+    k, v = G.history_bits(w)
+    ids = G.history_unit_ids(w)
+    assert k.shape == (4, w.cache_len, 64) and ids.shape == (w.cache_len,)
+    k1, _ = G.cache_unit_tokens(w, 1, range(4))
+    assert np.array_equal(k[:, 268:536], k1)
+    ks, _ = G.cache_unit_tokens(w, 2, range(4), 16)
+    assert np.array_equal(k[:, 536:], ks)
+    assert list(np.unique(ids[536:])) == [2] and list(np.unique(ids[268:536])) == [1]
+
+
+def test_data_scale_applied_before_rounding():
+    w = W.TINY
+    q, _, _, vel = G.step_tensors(w, 0)
+    qf = G.bf16_bits_to_f32(q)
+    assert 0.1 < qf.std() < 0.15                 # N(0,1)/8
+    assert 0.9 < G.bf16_bits_to_f32(vel).std() < 1.1
