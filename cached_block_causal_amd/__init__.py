@@ -1,0 +1,16 @@
+"""Cached block-causal denoising step for MI355X (gfx950).
+
+The computation lives in libws.so (hand-written HIP kernels behind the C ABI
+of include/ws.h). This package holds the kernel sources (csrc/), the build
+script and a thin PyTorch binding; importing the binding needs the built
+library and raises if it is missing.
+"""
+__all__ = ["KVCache", "kv_append", "block_causal_attn", "AttnCall", "attn_default_splits",
+           "attn_workspace_bytes", "fm_euler_step"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import ops
+        return getattr(ops, name)
+    raise AttributeError(name)

@@ -1,0 +1,308 @@
+// C ABI of libws: argument validation, split planning, kernel launches.
+// Every argument is checked before anything is enqueued; on failure nothing
+// is launched, caches keep their length, and ws_last_error() says why.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "ws.h"
+#include "ws_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ws_status fail(ws_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ws_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return WS_OK;
+  return fail(WS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+ws_status check_cache(const ws_kv_cache* c) {
+  if (!c) return fail(WS_ERR_NULL, "cache is NULL");
+  if (!head_dim_ok(c->head_dim))
+    return fail(WS_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->heads < 1) return fail(WS_ERR_SHAPE, "cache heads %d < 1", c->heads);
+  if (c->capacity < 0 || c->len < 0 || c->len > c->capacity)
+    return fail(WS_ERR_SHAPE, "cache len %d / capacity %d invalid", c->len, c->capacity);
+  if ((int64_t)c->heads * c->capacity * c->head_dim > ((int64_t)1 << 40))
+    return fail(WS_ERR_SHAPE, "cache larger than 2 TiB elements");
+  return WS_OK;
+}
+
+// Model of the split-KV pass used to pick a split count: each of `slots`
+// concurrent workgroups streams ceil(tiles / s) + 2 tiles (the 2 stand for Q
+// loads and the epilogue) at ~1.7 us per 128x64 tile at D = 128, in
+// ceil(items * s / slots) rounds, plus the partials' round trip through
+// memory at ~4 TB/s when s > 1.
+constexpr int kSlots = 256 * 2;  // 256 CUs x 2 resident workgroups
+constexpr int kMaxSplits = 256;
+
+int32_t default_splits(int32_t heads, int32_t n_q, int32_t head_dim, int64_t n_keys) {
+  if (heads <= 0 || n_q <= 0 || n_keys <= 0 || head_dim <= 0) return 1;
+  const int64_t items = (int64_t)heads * ((n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM);
+  const int64_t tiles = (n_keys + ws::kAttnBlockN - 1) / ws::kAttnBlockN;
+  const double t_tile_us = 1.7 * head_dim / 128.0;
+  int64_t max_s = tiles / 4;
+  if (max_s > kMaxSplits) max_s = kMaxSplits;
+  if (max_s < 1) max_s = 1;
+  int32_t best = 1;
+  double best_cost = 1e300;
+  for (int64_t s = 1; s <= max_s; ++s) {
+    const int64_t rounds = (items * s + kSlots - 1) / kSlots;
+    const int64_t per = (tiles + s - 1) / s;
+    double cost = (double)rounds * (double)(per + 2) * t_tile_us;
+    if (s > 1) cost += (double)s * heads * n_q * (head_dim + 1) * 4.0 * 2.0 / 4.0e6;
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = (int32_t)s;
+    }
+  }
+  return best;
+}
+
+size_t lse_offset(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits) {
+  const size_t o = (size_t)n_splits * heads * n_q * head_dim * sizeof(float);
+  return (o + 255) & ~(size_t)255;
+}
+
+size_t workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits) {
+  if (heads <= 0 || n_q <= 0 || head_dim <= 0 || n_splits <= 1) return 0;
+  return lse_offset(heads, n_q, head_dim, n_splits) + (size_t)n_splits * heads * n_q * sizeof(float);
+}
+
+struct AttnPlan {
+  ws::AttnArgs args;
+  int32_t splits;
+};
+
+// Validate a ws_block_causal_attn / ws_attn_partial call and fill the kernel
+// arguments. Returns WS_OK with plan->splits == 0 for a no-op (n_q == 0).
+ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const void* k_self,
+                    const void* v_self, int32_t n_self, int32_t n_units,
+                    const int32_t* q_unit_begin, const int32_t* unit_kend, float scale,
+                    int32_t n_splits, void* out, void* workspace, size_t workspace_bytes_in,
+                    AttnPlan* plan) {
+  ws_status st = check_cache(cache);
+  if (st != WS_OK) return st;
+  if (n_q < 0) return fail(WS_ERR_SHAPE, "n_q %d < 0", n_q);
+  if (n_self < 0) return fail(WS_ERR_SHAPE, "n_self %d < 0", n_self);
+  if (n_units < 1) return fail(WS_ERR_SHAPE, "n_units %d < 1", n_units);
+  if (n_units > WS_MAX_UNITS)
+    return fail(WS_ERR_UNSUPPORTED, "n_units %d > %d", n_units, WS_MAX_UNITS);
+  if (!q_unit_begin || !unit_kend) return fail(WS_ERR_NULL, "unit table is NULL");
+  if (q_unit_begin[0] != 0) return fail(WS_ERR_SHAPE, "q_unit_begin[0] = %d != 0", q_unit_begin[0]);
+  for (int32_t u = 0; u < n_units; ++u)
+    if (q_unit_begin[u + 1] < q_unit_begin[u])
+      return fail(WS_ERR_SHAPE, "q_unit_begin decreases at unit %d", u);
+  if (q_unit_begin[n_units] != n_q)
+    return fail(WS_ERR_SHAPE, "q_unit_begin[%d] = %d != n_q %d", n_units, q_unit_begin[n_units], n_q);
+  const int64_t n_keys = (int64_t)cache->len + n_self;
+  if (n_keys > 0x7FFFFFFF - ws::kAttnBlockN) return fail(WS_ERR_SHAPE, "too many keys");
+  for (int32_t u = 0; u < n_units; ++u) {
+    if (unit_kend[u] < 1 || unit_kend[u] > n_keys)
+      return fail(WS_ERR_SHAPE, "unit_kend[%d] = %d outside [1, %lld]", u, unit_kend[u],
+                  (long long)n_keys);
+    if (u > 0 && unit_kend[u] < unit_kend[u - 1])
+      return fail(WS_ERR_SHAPE, "unit_kend decreases at unit %d", u);
+  }
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(WS_ERR_SHAPE, "scale must be positive and finite");
+  if (n_splits < 0 || n_splits > kMaxSplits)
+    return fail(WS_ERR_SHAPE, "n_splits %d outside [0, %d]", n_splits, kMaxSplits);
+  const int32_t d = cache->head_dim;
+  const int32_t splits = n_splits ? n_splits : default_splits(cache->heads, n_q, d, n_keys);
+  if (n_q == 0) {
+    plan->splits = 0;
+    return WS_OK;
+  }
+  if (!q || !out) return fail(WS_ERR_NULL, "q or out is NULL");
+  if (cache->len > 0 && (!cache->k || !cache->v)) return fail(WS_ERR_NULL, "cache buffers are NULL");
+  if (n_self > 0 && (!k_self || !v_self)) return fail(WS_ERR_NULL, "k_self or v_self is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(cache->k) || !aligned16(cache->v) ||
+      !aligned16(k_self) || !aligned16(v_self))
+    return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");
+  const int64_t n_qtiles = (n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM;
+  const int64_t items = (int64_t)cache->heads * n_qtiles * splits;
+  if (items > 0x7FFFFFF0) return fail(WS_ERR_SHAPE, "too many work items");
+  if (splits > 1) {
+    const size_t need = workspace_bytes(cache->heads, n_q, d, splits);
+    if (!workspace) return fail(WS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes_in < need)
+      return fail(WS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_in, need);
+    if (!aligned16(workspace)) return fail(WS_ERR_ALIGN, "workspace is not 16-byte aligned");
+  }
+  ws::AttnArgs& a = plan->args;
+  memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(cache->k);
+  a.vc = static_cast<const uint16_t*>(cache->v);
+  a.ks = static_cast<const uint16_t*>(k_self);
+  a.vs = static_cast<const uint16_t*>(v_self);
+  a.out = static_cast<uint16_t*>(out);
+  if (splits > 1) {
+    char* wsb = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(wsb);
+    a.part_lse = reinterpret_cast<float*>(wsb + lse_offset(cache->heads, n_q, d, splits));
+  }
+  a.cache_head_stride = (int64_t)cache->capacity * d;
+  a.heads = cache->heads;
+  a.n_q = n_q;
+  a.len = cache->len;
+  a.n_self = n_self;
+  a.n_splits = splits;
+  a.n_qtiles = (int)n_qtiles;
+  a.n_items = (int)items;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_units = n_units;
+  for (int32_t u = 0; u <= n_units; ++u) a.q_unit_begin[u] = q_unit_begin[u];
+  for (int32_t u = 0; u < n_units; ++u) a.unit_kend[u] = unit_kend[u];
+  plan->splits = splits;
+  return WS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src, int32_t n_tok,
+                       int32_t src_heads, int32_t head_begin, int32_t layout, void* stream) {
+  g_last_error.clear();
+  ws_status st = check_cache(cache);
+  if (st != WS_OK) return st;
+  if (layout != WS_TOKEN_MAJOR && layout != WS_HEAD_MAJOR)
+    return fail(WS_ERR_UNSUPPORTED, "unknown source layout %d", layout);
+  if (n_tok < 0) return fail(WS_ERR_SHAPE, "n_tok %d < 0", n_tok);
+  if (src_heads < 1 || head_begin < 0 || (int64_t)head_begin + cache->heads > src_heads)
+    return fail(WS_ERR_SHAPE, "head block [%d, %lld) outside the %d source heads", head_begin,
+                (long long)head_begin + cache->heads, src_heads);
+  if ((int64_t)cache->len + n_tok > cache->capacity)
+    return fail(WS_ERR_CAPACITY, "len %d + n_tok %d > capacity %d", cache->len, n_tok,
+                cache->capacity);
+  if (n_tok == 0) return WS_OK;
+  if (!cache->k || !cache->v || !k_src || !v_src) return fail(WS_ERR_NULL, "a buffer is NULL");
+  if (!aligned16(cache->k) || !aligned16(cache->v) || !aligned16(k_src) || !aligned16(v_src))
+    return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");
+  st = hip_status(ws::launch_kv_append(static_cast<uint16_t*>(cache->k),
+                                       static_cast<uint16_t*>(cache->v),
+                                       static_cast<const uint16_t*>(k_src),
+                                       static_cast<const uint16_t*>(v_src), cache->heads,
+                                       cache->head_dim, cache->capacity, cache->len, n_tok,
+                                       src_heads, head_begin, layout,
+                                       static_cast<hipStream_t>(stream)),
+                  "kv_append launch");
+  if (st == WS_OK) cache->len += n_tok;
+  return st;
+}
+
+int32_t ws_attn_default_splits(int32_t heads, int32_t n_q, int32_t head_dim, int64_t n_keys) {
+  return default_splits(heads, n_q, head_dim, n_keys);
+}
+
+size_t ws_attn_workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits) {
+  return workspace_bytes(heads, n_q, head_dim, n_splits);
+}
+
+ws_status ws_attn_partial(const ws_kv_cache* cache, const void* q, int32_t n_q, const void* k_self,
+                          const void* v_self, int32_t n_self, int32_t n_units,
+                          const int32_t* q_unit_begin, const int32_t* unit_kend, float scale,
+                          int32_t n_splits, void* out, void* workspace, size_t workspace_bytes_in,
+                          void* stream) {
+  g_last_error.clear();
+  AttnPlan plan;
+  ws_status st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend,
+                           scale, n_splits, out, workspace, workspace_bytes_in, &plan);
+  if (st != WS_OK || plan.splits == 0) return st;
+  return hip_status(ws::launch_attn_partial(plan.args, cache->head_dim,
+                                            static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+ws_status ws_attn_merge(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits,
+                        const void* workspace, size_t workspace_bytes_in, void* out, void* stream) {
+  g_last_error.clear();
+  if (!head_dim_ok(head_dim)) return fail(WS_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", head_dim);
+  if (heads < 1 || n_q < 0) return fail(WS_ERR_SHAPE, "heads %d / n_q %d invalid", heads, n_q);
+  if (n_splits < 1 || n_splits > kMaxSplits)
+    return fail(WS_ERR_SHAPE, "n_splits %d outside [1, %d]", n_splits, kMaxSplits);
+  if (n_splits == 1 || n_q == 0) return WS_OK;
+  if ((int64_t)heads * n_q > 0x7FFFFFFF) return fail(WS_ERR_SHAPE, "too many rows");
+  const size_t need = workspace_bytes(heads, n_q, head_dim, n_splits);
+  if (!workspace) return fail(WS_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes_in < need)
+    return fail(WS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_in, need);
+  if (!out) return fail(WS_ERR_NULL, "out is NULL");
+  if (!aligned16(out) || !aligned16(workspace))
+    return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");
+  const char* wsb = static_cast<const char*>(workspace);
+  return hip_status(
+      ws::launch_attn_merge(reinterpret_cast<const float*>(wsb),
+                            reinterpret_cast<const float*>(wsb + lse_offset(heads, n_q, head_dim, n_splits)),
+                            static_cast<uint16_t*>(out), heads, n_q, head_dim, n_splits,
+                            static_cast<hipStream_t>(stream)),
+      "merge launch");
+}
+
+ws_status ws_block_causal_attn(const ws_kv_cache* cache, const void* q, int32_t n_q,
+                               const void* k_self, const void* v_self, int32_t n_self,
+                               int32_t n_units, const int32_t* q_unit_begin,
+                               const int32_t* unit_kend, float scale, int32_t n_splits, void* out,
+                               void* workspace, size_t workspace_bytes_in, void* stream) {
+  g_last_error.clear();
+  AttnPlan plan;
+  ws_status st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend,
+                           scale, n_splits, out, workspace, workspace_bytes_in, &plan);
+  if (st != WS_OK || plan.splits == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(ws::launch_attn_partial(plan.args, cache->head_dim, s), "attention launch");
+  if (st != WS_OK || plan.splits == 1) return st;
+  return hip_status(ws::launch_attn_merge(plan.args.part_o, plan.args.part_lse, plan.args.out,
+                                          cache->heads, n_q, cache->head_dim, plan.splits, s),
+                    "merge launch");
+}
+
+ws_status ws_fm_euler_step(float* x, const void* v, int64_t n, float dt, void* stream) {
+  g_last_error.clear();
+  if (n < 0) return fail(WS_ERR_SHAPE, "n %lld < 0", (long long)n);
+  if (!isfinite(dt)) return fail(WS_ERR_SHAPE, "dt is not finite");
+  if (n == 0) return WS_OK;
+  if (!x || !v) return fail(WS_ERR_NULL, "x or v is NULL");
+  if (!aligned16(x) || !aligned16(v)) return fail(WS_ERR_ALIGN, "x or v is not 16-byte aligned");
+  return hip_status(ws::launch_fm_euler(x, static_cast<const uint16_t*>(v), n, dt,
+                                        static_cast<hipStream_t>(stream)),
+                    "euler launch");
+}
+
+const char* ws_status_string(ws_status s) {
+  switch (s) {
+    case WS_OK: return "ok";
+    case WS_ERR_NULL: return "null pointer";
+    case WS_ERR_SHAPE: return "invalid size or table";
+    case WS_ERR_CAPACITY: return "cache capacity exceeded";
+    case WS_ERR_ALIGN: return "misaligned pointer";
+    case WS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case WS_ERR_WORKSPACE: return "workspace missing or too small";
+    case WS_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* ws_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

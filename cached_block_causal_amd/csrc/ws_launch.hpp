@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (internal to libws).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ws.h"
+
+namespace ws {
+
+// Cache append (bit copy of one head block of a slice into cache rows).
+hipError_t launch_kv_append(uint16_t* ck, uint16_t* cv, const uint16_t* sk, const uint16_t* sv,
+                            int heads, int head_dim, int capacity, int len, int n_tok,
+                            int src_heads, int head_begin, int layout, hipStream_t stream);
+
+// Euler update x = fma(dt, v, x).
+hipError_t launch_fm_euler(float* x, const uint16_t* v, int64_t n, float dt, hipStream_t stream);
+
+// Arguments of the split-KV attention pass (passed by value to the kernel).
+struct AttnArgs {
+  const uint16_t* q;        // [heads][n_q][D]
+  const uint16_t* kc;       // cache K [heads][capacity][D]
+  const uint16_t* vc;       // cache V
+  const uint16_t* ks;       // own-token K [heads][n_self][D]
+  const uint16_t* vs;       // own-token V
+  uint16_t* out;            // [heads][n_q][D]              (one split)
+  float* part_o;            // [splits][heads][n_q][D]      (several splits)
+  float* part_lse;          // [splits][heads][n_q]
+  int64_t cache_head_stride;  // capacity * D (elements)
+  int heads, n_q, len, n_self;
+  int n_splits, n_qtiles, n_items;
+  float scale_log2;         // softmax scale * log2(e)
+  int n_units;
+  int q_unit_begin[WS_MAX_UNITS + 1];
+  int unit_kend[WS_MAX_UNITS];
+};
+
+// Rows of queries one workgroup of the split-KV pass covers.
+constexpr int kAttnBlockM = 128;
+// Keys per LDS tile.
+constexpr int kAttnBlockN = 64;
+
+hipError_t launch_attn_partial(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_merge(const float* part_o, const float* part_lse, uint16_t* out,
+                             int heads, int n_q, int head_dim, int n_splits,
+                             hipStream_t stream);
+
+}  // namespace ws

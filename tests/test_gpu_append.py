@@ -1,0 +1,96 @@
+"""ws_kv_append on the GPU against the oracle's bit copy (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from workloads import gen as G
+from tests.gpu_common import POISON_BITS, dev_bits, host_bits, need_gpu, poisoned_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _poison_np(heads, cap, d):
+    return np.full((heads, cap, d), POISON_BITS, dtype=np.uint16)
+
+
+@pytest.mark.parametrize("w", W.ALL, ids=[w.name for w in W.ALL])
+def test_unit_append_bit_exact(w):
+    """The per-unit append of each workload: a full unit (slice + committed
+    latents) from an all-heads token-major source, keeping this GPU's block,
+    written behind existing rows; everything else keeps its bits."""
+    need_gpu()
+    from cached_block_causal_amd import kv_append
+    print(f"append {w.name}", flush=True)
+    d, hr = w.head_dim, w.heads
+    n = w.unit_tokens
+    start = 37                                   # rows already present
+    cap = start + n + 11                         # room after the append
+    cache = poisoned_cache(hr, d, cap)
+    pre_k, pre_v = G.cache_unit_tokens(w, 999, range(w.head_begin, w.head_begin + hr), start)
+    kv_append(cache, dev_bits(pre_k), dev_bits(pre_v), layout="head")
+    k, v = G.cache_unit_tokens(w, 5, range(w.heads_total), n)
+    ks, vs = G.token_major(k), G.token_major(v)
+    kv_append(cache, dev_bits(ks), dev_bits(vs), head_begin=w.head_begin, layout="token")
+    torch.cuda.synchronize()
+    assert cache.len == start + n
+    ek, ev, el = O.kv_append(_poison_np(hr, cap, d), _poison_np(hr, cap, d), 0, pre_k, pre_v, 0,
+                             O.HEAD_MAJOR)
+    ek, ev, el = O.kv_append(ek, ev, el, ks, vs, w.head_begin, O.TOKEN_MAJOR)
+    assert np.array_equal(host_bits(cache.k), ek)
+    assert np.array_equal(host_bits(cache.v), ev)
+
+
+def test_rank_share_head_blocks():
+    """Each of the 4 ranks of a 40-head slice receives its own 10 heads."""
+    need_gpu()
+    from cached_block_causal_amd import kv_append
+    w = W.V02_RANK
+    k, v = G.cache_unit_tokens(w, 3, range(40), w.slice_tokens)
+    ks, vs = G.token_major(k), G.token_major(v)
+    for r in range(4):
+        cache = poisoned_cache(10, 128, 64)
+        kv_append(cache, dev_bits(ks), dev_bits(vs), head_begin=10 * r)
+        got = host_bits(cache.k)
+        assert np.array_equal(got[:, :32], k[10 * r:10 * r + 10])
+        assert np.all(got[:, 32:] == POISON_BITS)
+        assert np.array_equal(host_bits(cache.v)[:, :32], v[10 * r:10 * r + 10])
+
+
+def test_history_by_appends_equals_generator():
+    """Building the tiny workload's cache unit by unit gives the construction
+    log's contents."""
+    need_gpu()
+    from tests.gpu_common import fill_history
+    w = W.TINY
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    k, v = G.history_bits(w)
+    assert cache.len == w.cache_len
+    assert np.array_equal(host_bits(cache.k)[:, :w.cache_len], k)
+    assert np.array_equal(host_bits(cache.v)[:, :w.cache_len], v)
+    assert np.all(host_bits(cache.k)[:, w.cache_len:] == POISON_BITS)
+
+
+def test_overflow_is_rejected_without_writes():
+    need_gpu()
+    from cached_block_causal_amd import kv_append
+    from cached_block_causal_amd._lib import WS_ERR_CAPACITY, WsError
+    cache = poisoned_cache(2, 64, 10)
+    src = dev_bits(np.arange(11 * 2 * 64, dtype=np.uint16).reshape(11, 2, 64))
+    with pytest.raises(WsError) as e:
+        kv_append(cache, src, src)
+    assert e.value.status == WS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert cache.len == 0
+    assert np.all(host_bits(cache.k) == POISON_BITS)
+
+
+def test_empty_append_is_noop():
+    need_gpu()
+    from cached_block_causal_amd import kv_append
+    cache = poisoned_cache(2, 128, 4)
+    src = dev_bits(np.zeros((0, 2, 128), dtype=np.uint16))
+    kv_append(cache, src, src)
+    assert cache.len == 0

@@ -1,0 +1,152 @@
+"""ws_block_causal_attn on the GPU against the fp64 oracle, on every workload.
+
+Small workloads are compared on every output element; the full-size ones on
+every output of sampled heads (the oracle computes each head independently).
+Unused cache capacity is poisoned with NaN, so any read past the valid rows
+would show up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from workloads import gen as G
+from tests.gpu_common import (assert_close, dev_bits, fill_history, host_bits, need_gpu,
+                              poisoned_cache)
+
+pytestmark = pytest.mark.gpu
+
+
+def _streaming_case(w, steps, heads_sampled=None):
+    """Run the streaming step of workload w on the GPU for the given denoise
+    steps; compare all heads (heads_sampled None) or the sampled heads."""
+    from cached_block_causal_amd import AttnCall
+    print(f"attn {w.name} steps {steps} heads {heads_sampled}", flush=True)
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    assert cache.len == w.cache_len
+    hist_heads = (list(range(w.head_begin, w.head_begin + w.heads)) if heads_sampled is None
+                  else [w.head_begin + h for h in heads_sampled])
+    hk, hv = G.history_bits(w, hist_heads)
+    ids = G.history_unit_ids(w)
+    sel = slice(None) if heads_sampled is None else list(heads_sampled)
+    results = []
+    for s in steps:
+        q, ks, vs, _ = G.step_tensors(w, s)
+        call = AttnCall(cache, dev_bits(q), dev_bits(ks), dev_bits(vs))
+        out = host_bits(call.run())
+        # the two-launch form gives the same bits
+        call.out.view(torch.int16).fill_(0x7FC0)
+        call.partial()
+        call.merge()
+        assert np.array_equal(host_bits(call.out), out)
+        k, v, ku = O.streaming_keys(hk, hv, w.cache_len, ids, ks[sel], vs[sel], w.current_unit)
+        want = O.attention(q[sel], k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(w.head_dim))
+        results.append(assert_close(out[sel], want, f"{w.name} step {s}"))
+    print(results, flush=True)
+
+
+def test_tiny_streaming_all_steps():
+    need_gpu()
+    _streaming_case(W.TINY, range(4))
+
+
+def test_v01_unit_full():
+    need_gpu()
+    _streaming_case(W.V01_UNIT, [0, 3])
+
+
+@pytest.mark.timeout(300)
+def test_v02_rank_share_sampled_heads():
+    need_gpu()
+    _streaming_case(W.V02_RANK, [0], heads_sampled=[0, 9])
+
+
+@pytest.mark.timeout(300)
+def test_v02_whole_performer_sampled_heads():
+    need_gpu()
+    _streaming_case(W.V02_WHOLE, [0], heads_sampled=[0, 21, 39])
+
+
+@pytest.mark.timeout(600)
+def test_audio_long_history_sampled_heads():
+    need_gpu()
+    _streaming_case(W.AUDIO_LONG, [0, 3], heads_sampled=[0, 13, 39])
+
+
+def _multi_unit_tiny():
+    """The tiny workload in its multi-unit form: all three units' tokens in
+    the cache, queries of all three units, unit u seeing units <= u."""
+    w = W.TINY
+    n_units = w.cached_units + 1
+    ks = [G.cache_unit_tokens(w, u, range(w.heads)) for u in range(n_units)]
+    ck = np.concatenate([k for k, _ in ks], axis=1)
+    cv = np.concatenate([v for _, v in ks], axis=1)
+    q = np.concatenate([G.step_tensors(w, 0, unit=u)[0] for u in range(n_units)], axis=1)
+    ku = np.repeat(np.arange(n_units), w.unit_tokens)
+    qu = np.repeat(np.arange(n_units), w.video_tokens)
+    qb = [w.video_tokens * u for u in range(n_units + 1)]
+    kend = [w.unit_tokens * (u + 1) for u in range(n_units)]
+    return w, ck, cv, q, ku, qu, qb, kend
+
+
+def _run_multi(w, ck, cv, q, qb, kend, n_splits=0):
+    from cached_block_causal_amd import block_causal_attn, kv_append
+    cache = poisoned_cache(w.heads, w.head_dim, ck.shape[1] + 40)
+    kv_append(cache, dev_bits(ck), dev_bits(cv), layout="head")
+    return host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=qb, unit_kend=kend,
+                                       n_splits=n_splits))
+
+
+@pytest.mark.parametrize("n_splits", [0, 1, 4])
+def test_tiny_multi_unit_block_causal(n_splits):
+    need_gpu()
+    w, ck, cv, q, ku, qu, qb, kend = _multi_unit_tiny()
+    out = _run_multi(w, ck, cv, q, qb, kend, n_splits)
+    want = O.attention(q, ck, cv, qu, ku, 1 / np.sqrt(w.head_dim))
+    assert_close(out, want, f"multi-unit splits {n_splits}")
+
+
+def test_later_unit_changes_leave_earlier_outputs_bit_identical():
+    need_gpu()
+    w, ck, cv, q, ku, qu, qb, kend = _multi_unit_tiny()
+    base = _run_multi(w, ck, cv, q, qb, kend)
+    ck2, cv2 = ck.copy(), cv.copy()
+    late = ku == 2
+    big = G.bf16_rne_bits(np.where(np.arange(w.head_dim) % 2 == 0, 1e4, -1e4).astype(np.float32))
+    ck2[:, late] = big
+    cv2[:, late] = G.bf16_rne_bits(np.array([123.0], np.float32))[0]
+    pert = _run_multi(w, ck2, cv2, q, qb, kend)
+    early = qu < 2
+    assert np.array_equal(base[:, early], pert[:, early])
+    assert not np.array_equal(base[:, ~early], pert[:, ~early])
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 7, 33])
+def test_split_counts_agree_with_oracle(n_splits):
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    w = W.V01_UNIT
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    q, ks, vs, _ = G.step_tensors(w, 1)
+    out = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(ks), dev_bits(vs),
+                                      n_splits=n_splits))
+    hk, hv = G.history_bits(w, [0, 23])
+    k, v, ku = O.streaming_keys(hk, hv, w.cache_len, G.history_unit_ids(w), ks[[0, 23]],
+                                vs[[0, 23]], w.current_unit)
+    want = O.attention(q[[0, 23]], k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(128))
+    assert_close(out[[0, 23]], want, f"splits {n_splits}")
+
+
+def test_repeated_runs_are_bit_identical():
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    w = W.V01_UNIT
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    q, ks, vs, _ = G.step_tensors(w, 2)
+    a = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(ks), dev_bits(vs)))
+    b = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(ks), dev_bits(vs)))
+    assert np.array_equal(a, b)

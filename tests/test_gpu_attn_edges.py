@@ -1,0 +1,134 @@
+"""Edge cases of ws_block_causal_attn on the GPU: special values, ragged
+sizes, partial visibility of the cache, empty inputs and error paths."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import gen as G
+from tests.gpu_common import assert_close, dev_bits, host_bits, need_gpu, poisoned_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(rng, shape, scale=1.0):
+    return G.bf16_rne_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def _cache_with(ck, cv, extra=17):
+    from cached_block_causal_amd import kv_append
+    h, n, d = ck.shape
+    cache = poisoned_cache(h, d, n + extra)
+    if n:
+        kv_append(cache, dev_bits(ck), dev_bits(cv), layout="head")
+    return cache
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_splits", [0, 1, 3])
+def test_single_visible_key_returns_v_bit_exact(d, n_splits):
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(d)
+    ck, cv = _bits(rng, (3, 70, d)), _bits(rng, (3, 70, d))
+    q = _bits(rng, (3, 5, d))
+    cache = _cache_with(ck, cv)
+    out = host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=[0, 5], unit_kend=[1],
+                                      n_splits=n_splits))
+    assert np.array_equal(out, np.broadcast_to(cv[:, :1], out.shape))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_identical_keys_give_mean_of_values(d):
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(1)
+    row = _bits(rng, (d,))
+    ck = np.broadcast_to(row, (2, 300, d)).copy()
+    cv = _bits(rng, (2, 300, d))
+    q = _bits(rng, (2, 40, d))
+    cache = _cache_with(ck, cv)
+    out = host_bits(block_causal_attn(cache, dev_bits(q)))
+    want = np.broadcast_to(O.bf16_to_f64(cv).mean(axis=1, keepdims=True), (2, 40, d))
+    assert_close(out, want, "identical keys")
+
+
+RAGGED = [
+    # (d, heads, n_q, n_cache, n_self)
+    (64, 3, 1, 1, 0),
+    (64, 2, 31, 63, 5),
+    (128, 2, 33, 65, 0),
+    (128, 1, 129, 0, 200),
+    (64, 5, 300, 500, 77),
+    (128, 3, 257, 1000, 129),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[str(c) for c in RAGGED])
+def test_ragged_streaming_sizes(case):
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    d, h, nq, nc, ns = case
+    rng = np.random.default_rng(nq * 7 + nc)
+    ck, cv = _bits(rng, (h, nc, d)), _bits(rng, (h, nc, d))
+    q = _bits(rng, (h, nq, d))
+    sk, sv = _bits(rng, (h, ns, d)), _bits(rng, (h, ns, d))
+    cache = _cache_with(ck, cv)
+    out = torch.full((h, nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    block_causal_attn(cache, dev_bits(q), dev_bits(sk) if ns else None,
+                      dev_bits(sv) if ns else None, out=out)
+    k = np.concatenate([ck, sk], axis=1)
+    v = np.concatenate([cv, sv], axis=1)
+    want = O.attention(q, k, v, np.zeros(nq), np.zeros(nc + ns), 1 / np.sqrt(d))
+    assert_close(host_bits(out), want, str(case))
+
+
+def test_units_seeing_part_of_the_cache():
+    """Several query units whose visible ranges end inside the cache, inside
+    the own tokens, and mid-tile, with an empty unit in between."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(5)
+    d, h, nc, ns = 128, 2, 400, 90
+    ck, cv = _bits(rng, (h, nc, d)), _bits(rng, (h, nc, d))
+    sk, sv = _bits(rng, (h, ns, d)), _bits(rng, (h, ns, d))
+    qb = [0, 70, 70, 200, 333]
+    kend = [130, 250, 401, 490]
+    q = _bits(rng, (h, qb[-1], d))
+    cache = _cache_with(ck, cv)
+    for n_splits in (0, 1, 5):
+        out = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(sk), dev_bits(sv),
+                                          q_unit_begin=qb, unit_kend=kend, n_splits=n_splits))
+        k = np.concatenate([ck, sk], axis=1)
+        v = np.concatenate([cv, sv], axis=1)
+        # visibility by key index: key j carries unit id = first unit whose kend > j
+        key_unit = np.searchsorted(np.array(kend), np.arange(nc + ns), side="right")
+        q_unit = np.concatenate([np.full(qb[u + 1] - qb[u], u) for u in range(len(kend))])
+        want = O.attention(q, k, v, q_unit, key_unit, 1 / np.sqrt(d))
+        assert_close(out, want, f"partial visibility splits {n_splits}")
+
+
+def test_empty_query_set_is_noop():
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(0)
+    cache = _cache_with(_bits(rng, (2, 10, 64)), _bits(rng, (2, 10, 64)))
+    q = torch.empty((2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    out = block_causal_attn(cache, q)
+    assert out.shape == (2, 0, 64)
+
+
+def test_errors_are_reported_before_launch():
+    need_gpu()
+    from cached_block_causal_amd import AttnCall, block_causal_attn
+    from cached_block_causal_amd._lib import WS_ERR_SHAPE, WS_ERR_WORKSPACE, WsError
+    rng = np.random.default_rng(0)
+    cache = _cache_with(_bits(rng, (2, 300, 64)), _bits(rng, (2, 300, 64)))
+    q = dev_bits(_bits(rng, (2, 50, 64)))
+    with pytest.raises(WsError) as e:                       # kend beyond the keys
+        block_causal_attn(cache, q, q_unit_begin=[0, 50], unit_kend=[301])
+    assert e.value.status == WS_ERR_SHAPE
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(WsError) as e:
+        AttnCall(cache, q, n_splits=4, workspace=small).run()
+    assert e.value.status == WS_ERR_WORKSPACE
