@@ -1,0 +1,239 @@
+"""Benchmark of one streaming unit of the cached block-causal denoising step.
+
+One step = one 160 ms streaming unit on this GPU's share of the work:
+  1. ws_kv_append of the thinker's K/V slice (token-major, all heads of the
+     slice, keeping this GPU's head block),
+  2. for each denoise step: ws_attn_partial + ws_attn_merge (block-causal
+     attention of the unit's latent queries over the cache plus the unit's own
+     tokens) and ws_fm_euler_step (x += dt * v),
+  3. ws_kv_append of the unit's generated latent K/V (head-major commit).
+The cache length is rewound to the same history before every step, so every
+step is the same workload. All inputs are resident in HBM before timing.
+
+Prints one JSON line. `value` is attention TFLOP/s over the whole unit (all
+denoise steps' algorithmic attention FLOPs / wall time of the unit);
+`roofline` is the split-KV attention kernel against the bf16 MFMA peak, its
+duration measured with HIP events around each launch on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+UNIT_BUDGET_MS = 160.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "cached_block_causal_amd", "csrc", "attn_fwd.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="v02_rank_share")
+    p.add_argument("--splits", type=int, default=0, help="0 = library default")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain copy (the append kernel) of known size, for "
+                        "calibrating HBM byte counters")
+    return p.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from committed counter
+    runs, only if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of the same workload: whole
+    heads of denoise step 0 (all query rows over all keys), as many as fit
+    in about budget_s seconds, on the host's cores."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import gen as G
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count() or 1
+    ids = G.history_unit_ids(w)
+    heads_done, flops, elapsed = 0, 0, 0.0
+    for h in range(w.heads):
+        head = [w.head_begin + h]
+        hk, hv = G.history_bits(w, head)
+        q, ks, vs, _ = G.step_tensors(w, 0, heads=head)
+        t0 = time.perf_counter()
+        k, v, ku = O.streaming_keys(hk, hv, w.cache_len, ids, ks, vs, w.current_unit)
+        O.attention(q, k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(w.head_dim))
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        flops += 4 * w.head_dim * w.n_q * w.n_keys
+        if elapsed >= budget_s:
+            break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, attention of denoise step 0 for {heads_done} of "
+                      f"{w.heads} heads ({w.n_q} queries x {w.n_keys} keys each), "
+                      f"{elapsed:.2f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def calib_copy(steps: int) -> None:
+    """Append kernel over a large slice: a plain copy of known size."""
+    import torch
+
+    from cached_block_causal_amd import KVCache, kv_append
+    heads, d, n = 40, 128, 16384
+    cache = KVCache(heads, d, n)
+    src_k = torch.zeros((n, heads, d), dtype=torch.bfloat16, device="cuda")
+    src_v = torch.zeros_like(src_k)
+    for _ in range(steps):
+        cache.rewind(0)
+        kv_append(cache, src_k, src_v)
+    torch.cuda.synchronize()
+    nbytes = 2 * n * heads * d * 2
+    print(json.dumps({"calib_copy": True, "read_bytes_per_launch": nbytes,
+                      "write_bytes_per_launch": nbytes, "launches": steps}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU Ulysses exchange is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+    from cached_block_causal_amd import AttnCall, KVCache, fm_euler_step, kv_append
+    from workloads import gen as G
+    from workloads.device import dev_bits
+
+    if args.calib_copy:
+        calib_copy(args.steps)
+        return
+
+    w = W.BY_NAME[args.workload]
+    heads = list(range(w.head_begin, w.head_begin + w.heads))
+    t_setup = time.perf_counter()
+    cache = KVCache(w.heads, w.head_dim, w.capacity)
+    for u in range(w.cached_units):                      # history (untimed)
+        k, v = G.cache_unit_tokens(w, u, heads)
+        kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
+    history_len = cache.len
+    sk, sv = G.cache_unit_tokens(w, w.current_unit, range(w.heads_total), w.slice_tokens)
+    slice_k, slice_v = dev_bits(G.token_major(sk)), dev_bits(G.token_major(sv))
+    kv_append(cache, slice_k, slice_v, head_begin=w.head_begin)
+    steps_in = [G.step_tensors(w, s) for s in range(w.steps)]
+    dq = [dev_bits(t[0]) for t in steps_in]
+    dks = [dev_bits(t[1]) for t in steps_in]
+    dvs = [dev_bits(t[2]) for t in steps_in]
+    dvel = [dev_bits(t[3]) for t in steps_in]
+    x = torch.from_numpy(G.x0(w)).to("cuda")
+    calls = [AttnCall(cache, dq[0], dks[0], dvs[0], n_splits=args.splits)]
+    calls += [AttnCall(cache, dq[s], dks[s], dvs[s], n_splits=args.splits,
+                       workspace=calls[0].workspace)      # one workspace for all steps
+              for s in range(1, w.steps)]
+    splits = calls[0].splits
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    n_attn = args.steps * w.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_attn)]
+
+    def unit_step(timed_events=None):
+        cache.rewind(history_len)
+        kv_append(cache, slice_k, slice_v, head_begin=w.head_begin)
+        for s in range(w.steps):
+            if timed_events is not None:
+                timed_events[s][0].record()
+            calls[s].partial()
+            if timed_events is not None:
+                timed_events[s][1].record()
+            calls[s].merge()
+            fm_euler_step(x, dvel[s], w.dt)
+        kv_append(cache, dks[-1], dvs[-1], layout="head")   # commit the unit's latents
+
+    for _ in range(args.warmup):
+        unit_step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        unit_step(ev[i * w.steps:(i + 1) * w.steps])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+
+    flops_step = w.attn_flops()
+    value = flops_step * w.steps / (ms_per_step * 1e-3) / 1e12
+    achieved = flops_step / (attn_avg_ms * 1e-3) / 1e12
+    traffic = stored_traffic(w.name)
+    out = {
+        "metric": "attention TFLOP/s per 160 ms unit (4 denoise steps), with % of bf16 MFMA "
+                  "peak per denoise step and us/unit vs the 160 ms budget",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) Q/K/V/velocity, fp32 N(0,1) latent)",
+        "config": {"workload": w.name, "heads": w.heads, "heads_total": w.heads_total,
+                   "head_dim": w.head_dim, "n_q": w.n_q, "cache_len": w.cache_len,
+                   "n_keys": w.n_keys, "denoise_steps": w.steps, "splits": splits,
+                   "slice_tokens": w.slice_tokens, "commit_tokens": w.n_self},
+        "roofline": {"kernel": "attn_partial_kernel<%d>" % w.head_dim, "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "launch_ms_avg": round(attn_avg_ms, 5),
+                     "launch_ms_min": round(min(attn_ms), 5)},
+        "us_per_unit": round(ms_per_step * 1e3, 1),
+        "unit_budget_frac": round(ms_per_step / UNIT_BUDGET_MS, 5),
+        "attention_layers_per_unit_budget": int(UNIT_BUDGET_MS // ms_per_step),
+        "host_wall_s": round(wall, 3),
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

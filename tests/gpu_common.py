@@ -6,6 +6,7 @@ import torch
 
 import oracle as O
 from workloads import gen as G
+from workloads.device import dev_bits, host_bits  # noqa: F401
 
 # bf16 quiet NaN used to poison unused cache capacity and guard bands
 POISON_BITS = 0x7FC0
@@ -17,16 +18,6 @@ REL_FRO = 5e-3
 def need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def dev_bits(a: np.ndarray) -> torch.Tensor:
-    """uint16 bf16 bits -> contiguous bfloat16 tensor on cuda:0."""
-    a = np.ascontiguousarray(a, dtype=np.uint16)
-    return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
-
-
-def host_bits(t: torch.Tensor) -> np.ndarray:
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 def poisoned_cache(heads, head_dim, capacity):
