@@ -14,23 +14,26 @@
 //    so the row max is a per-lane max plus one exchange with lane ^ 32, and
 //    the probabilities are already in the B-operand layout of O^T = V^T P^T:
 //    P never leaves registers.
-//  * V is staged in LDS transposed (V^T, dims x keys) with the keys of each
-//    16-key group permuted (bits 2 and 3 of the key index swapped) so that a
-//    lane's eight B-operand keys of P are contiguous in V^T: the A operand of
-//    the PV product is one 16-byte LDS read. The transpose happens once per
-//    tile while writing LDS (4-key x 8-dim register blocks, v_perm).
+//  * K and V tiles of 64 keys go from global memory straight into LDS (buffer
+//    loads with the LDS-destination bit: no staging registers), in natural
+//    row order. A row is cut into 64-byte column groups of four 16-byte
+//    chunks; the chunk slot inside a group is XOR-swizzled with bits 2-3 of
+//    the row, so the 32 rows one MFMA operand read touches spread over all
+//    LDS banks. The V^T operand of the PV product comes from the LDS
+//    transpose read ds_read_b64_tr_b16 (two per MFMA), which hands each lane
+//    4 keys of one dimension.
 //  * Online softmax in the exp2 domain, fp32, with the running max allowed to
 //    lag the true max by up to 2^8 before O and l are rescaled (rescales are
 //    rare once the max settles; the result is the same up to rounding).
 //  * Software pipeline over 64-key tiles: while the vector unit runs the
-//    softmax of tile t, the matrix cores already compute S^T of tile t+1, then
-//    O^T += V^T P^T of tile t. K and V^T each have two LDS stages (72 KB at
-//    D = 128, so two workgroups fit in a CU's 160 KB); K is written two tiles
-//    ahead and V one tile ahead, which needs one barrier per tile. Global
-//    loads are issued a tile before use. A tile never straddles the cache and
-//    the own tokens; its rows are read with raw buffer loads at per-thread
-//    constant offsets from a resource built per tile with scalar instructions,
-//    whose range ends at the tile's last valid row (zeros past it).
+//    softmax of tile t, the matrix cores compute S^T of tile t+1 (their order
+//    is fixed with scheduling barriers), then O^T += V^T P^T of tile t. K and
+//    V each have two LDS stages (64 KB at D = 128, two workgroups per CU); the
+//    loads of K(t+2) and V(t+1) are issued when tile t starts and awaited at
+//    its end, one barrier per tile. A tile never straddles the cache and the
+//    own tokens; its rows are read through a buffer resource built per tile
+//    with scalar instructions whose range ends at the tile's last valid row,
+//    so missing rows read as zeros.
 //  * Work items (head, split, query tile) are ordered with the query tile
 //    fastest and mapped onto blockIdx so that the items of one (head, split)
 //    land on the same XCD (workgroups are dispatched round-robin over the 8
@@ -51,24 +54,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D>
 struct Tile {
-  static constexpr int kKPitch = D + 8;              // bf16 per K row in LDS
-  static constexpr int kVPitch = kAttnBlockN + 8;    // bf16 per V^T row
-  static constexpr int kKElems = kAttnBlockN * kKPitch;
-  static constexpr int kVElems = D * kVPitch;
-  static constexpr int kStage = kKElems + kVElems;
-  static constexpr int kKChunks = kAttnBlockN * (D / 8) / kThreads;  // per thread
-  static constexpr int kVTasks = (kAttnBlockN / 4) * (D / 8);         // 4 keys x 8 dims each
+  static constexpr int kGroups = D / 32;                  // 64-byte column groups per row
+  static constexpr int kGroupBytes = kAttnBlockN * 64;    // one group of a 64-row tile
+  static constexpr int kStageBytes = kGroups * kGroupBytes;
   static constexpr int kDSteps = D / 16;   // k-steps of the QK^T product
   static constexpr int kDBlocks = D / 32;  // 32-dim blocks of O^T
-  static_assert(kKChunks * kThreads == kAttnBlockN * (D / 8), "K tile split");
-  static_assert(kVTasks <= kThreads, "V tile split");
+  static_assert(kGroups == 2 || kGroups == 4, "head_dim 64 or 128");
 };
 
-// Position of a key (within a 64-key tile) in a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int key) {
-  const int b = ((key >> 2) ^ (key >> 3)) & 1;
-  return key ^ (b * 12);
-}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Visible-key count of a query row from the unit table.
 __device__ __forceinline__ int row_kend(const AttnArgs& a, int row) {
@@ -77,12 +72,36 @@ __device__ __forceinline__ int row_kend(const AttnArgs& a, int row) {
   return a.unit_kend[u];
 }
 
+// Column group G (byte offset G*64 within each row, passed as the scalar
+// offset: the row offset stays in voff, so a row past the range still reads
+// zeros) of a tile's rows into LDS at dst: lane l writes dst + 16*l. The
+// instruction's immediate offset is left at 0 because it also moves the LDS
+// destination.
+template <int G>
+__device__ __forceinline__ void dma_group(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, G * 64, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(base + byte_off);
+}
+
+// 4 bf16 of one dimension from 4 consecutive V rows (LDS transpose read)
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArgs a) {
   using T = Tile<D>;
-  // two K stages then two V^T stages
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::kKElems + 2 * T::kVElems];
+  // separate objects per stage, so memory dependences between the in-flight
+  // global->LDS loads and the reads of the other stages are visibly absent
+  __shared__ __attribute__((aligned(16))) char k_st0[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char k_st1[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char v_st0[T::kStageBytes];
+  __shared__ __attribute__((aligned(16))) char v_st1[T::kStageBytes];
 
   // ---- work item: XCD-aware decode of (head, split, query tile)
   const int per_xcd = gridDim.x >> 3;
@@ -95,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lrow = lane & 31;
   const int half = lane >> 5;
 
@@ -141,21 +160,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   float m_run = kNegInf;  // running max of scaled scores (log2 units)
   float l_run = 0.f;      // this lane's share of the softmax denominator
 
-  // ---- per-thread constant offsets of the tile staging
-  // K: rows kKChunks*(tid / (D/8)) + i, 16-byte column tid % (D/8)
-  const int k_row0 = T::kKChunks * (tid / (D / 8));  // rows k_row0 + i: resource i starts i rows in
-  const int k_col = tid % (D / 8);
-  const uint32_t k_goff = (uint32_t)(k_row0 * D + k_col * 8) * 2;
-  const int k_loff = k_row0 * T::kKPitch + k_col * 8;
-  // V: rows 4*vg + jj, 16-byte column vc, written transposed
-  const int vg = tid & 15;
-  const int vc = tid >> 4;
-  const bool v_task = T::kVTasks == kThreads || tid < T::kVTasks;
-  const uint32_t v_goff = (uint32_t)(4 * vg * D + vc * 8) * 2;
-  const int v_loff = vc * 8 * T::kVPitch + vt_pos(4 * vg);
+  // ---- LDS layout: byte (G, row, slot) = G * kGroupBytes + row * 64 + slot * 16
+  // holds 16-byte chunk 4*G + (slot ^ ((row >> 2) & 3)) of the row.
+  // DMA: wave w moves rows 16w .. 16w+15; lane l writes row 16w + l/4, slot l%4.
+  const uint32_t dma_off = (uint32_t)((16 * wave + (lane >> 2)) * D * 2 + (((lane & 3) ^ (lane >> 4)) * 16));
+  // K operand of MFMA (kb, ks): row kb*32 + lrow, chunk 2*ks + half
+  const int k_ofs[2] = {lrow * 64 + (((0 + half) ^ ((lrow >> 2) & 3)) * 16),
+                        lrow * 64 + (((2 + half) ^ ((lrow >> 2) & 3)) * 16)};
+  // V^T operand of MFMA (db, kb, ks2), read e (keys +8e): lane 16g + 4s + q
+  // reads row kb*32 + 16*ks2 + 8e + 4*half + s, dims db*32 + 16*(g&1) + 4q ..
+  const int v_s = (lane >> 2) & 3, v_q = lane & 3, v_g1 = (lane >> 4) & 1;
+  const int v_u = 2 * v_g1 + (v_q >> 1);
+  const int v_ofs[2] = {(4 * half + v_s) * 64 + ((v_u ^ (0 + half)) * 16) + 8 * (v_q & 1),
+                        (4 * half + v_s) * 64 + ((v_u ^ (2 + half)) * 16) + 8 * (v_q & 1)};
 
-  uint16_t* const kst[2] = {smem, smem + T::kKElems};
-  uint16_t* const vst[2] = {smem + 2 * T::kKElems, smem + 2 * T::kKElems + T::kVElems};
+  char* const kst[2] = {k_st0, k_st1};
+  char* const vst[2] = {v_st0, v_st1};
 
   // tile r: position in the key sequence, valid rows, and segment row pointers
   struct TileLoc {
@@ -168,175 +188,151 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     const int local = (own ? t - n_ct : t) * kAttnBlockN;
     TileLoc L;
     L.abs_base = own ? a.len + local : local;
-    L.rows = min(kAttnBlockN, (own ? self_rows : cache_rows) - local);
+    // rows <= 0 past the end of the split: an empty range, loads read zeros.
+    // (The clamp would otherwise become a VALU med3, making the resource look
+    // per-lane and every load a waterfall loop.)
+    L.rows = __builtin_amdgcn_readfirstlane(max(0, min(kAttnBlockN, (own ? self_rows : cache_rows) - local)));
     L.k = (own ? ks_h : kc_h) + (int64_t)local * D;
     L.v = (own ? vs_h : vc_h) + (int64_t)local * D;
     return L;
   };
-  // resource over rows [first, L.rows) of a tile, starting at row `first`
-  auto row_rsrc = [&](const uint16_t* tile, int rows, int first) {
-    const int n = max(rows - first, 0);
-    return buffer_rsrc(tile + first * D, (uint32_t)n * D * 2);
-  };
-  u32x4 kreg[T::kKChunks];
-  u32x4 vreg[4];
-  auto load_k = [&](int r) {
-    const TileLoc L = locate(r);
-#pragma unroll
-    for (int i = 0; i < T::kKChunks; ++i) kreg[i] = buffer_load16(row_rsrc(L.k, L.rows, i), k_goff);
-  };
-  auto load_v = [&](int r) {
-    const TileLoc L = locate(r);
-    if (v_task) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) vreg[jj] = buffer_load16(row_rsrc(L.v, L.rows, jj), v_goff);
+  // this wave's share of a tile: rows 16w.. of every column group, into LDS
+  auto dma_tile = [&](const uint16_t* rows_ptr, int rows, char* stage) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows_ptr, (uint32_t)rows * D * 2);
+    char* dst = stage + wave * 1024;
+    dma_group<0>(rs, dst, dma_off);
+    dma_group<1>(rs, dst + T::kGroupBytes, dma_off);
+    if constexpr (T::kGroups == 4) {
+      dma_group<2>(rs, dst + 2 * T::kGroupBytes, dma_off);
+      dma_group<3>(rs, dst + 3 * T::kGroupBytes, dma_off);
     }
   };
-  auto store_k = [&](uint16_t* stage) {
-#pragma unroll
-    for (int i = 0; i < T::kKChunks; ++i)
-      *reinterpret_cast<u32x4*>(stage + k_loff + i * T::kKPitch) = kreg[i];
+  auto dma_k = [&](int r, char* stage) {
+    const TileLoc L = locate(r);
+    dma_tile(L.k, L.rows, stage);
   };
-  auto store_v = [&](uint16_t* stage) {
-    if (v_task) {
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        *reinterpret_cast<u32x2*>(stage + v_loff + (2 * wd) * T::kVPitch) =
-            u32x2{lo_halves(vreg[0][wd], vreg[1][wd]), lo_halves(vreg[2][wd], vreg[3][wd])};
-        *reinterpret_cast<u32x2*>(stage + v_loff + (2 * wd + 1) * T::kVPitch) =
-            u32x2{hi_halves(vreg[0][wd], vreg[1][wd]), hi_halves(vreg[2][wd], vreg[3][wd])};
-      }
-    }
+  auto dma_v = [&](int r, char* stage) {
+    const TileLoc L = locate(r);
+    dma_tile(L.v, L.rows, stage);
+  };
+  auto k_frag = [&](const char* kstage, int kb, int ks) {
+    return lds_read16(kstage, (ks >> 1) * T::kGroupBytes + kb * 32 * 64 + k_ofs[ks & 1]);
+  };
+  auto v_frag = [&](const char* vstage, int i) {  // i = (db, kb, ks2) with ks2 fastest
+    const int db = i >> 2, kb = (i >> 1) & 1, ks2 = i & 1;
+    const char* b = vstage + db * T::kGroupBytes + (kb * 32 + 16 * ks2) * 64;
+    const u32x2 lo = lds_read_tr(b, v_ofs[0]);
+    const u32x2 hi = lds_read_tr(b + 8 * 64, v_ofs[1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
   // S^T of one 64-key tile from an LDS K stage
-  auto qk = [&](const uint16_t* kstage, f32x16 (&s)[2]) {
-    const uint16_t* lk = kstage + lrow * T::kKPitch + 8 * half;
+  auto qk = [&](const char* kstage, f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < T::kDSteps; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + kb * 32 * T::kKPitch + ks * 16);
-        s[kb] = mfma32x32x16(ka, qf[ks], s[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(k_frag(kstage, kb, ks), qf[ks], s[kb]);
+  };
+  // the tile's global loads into LDS are complete for this wave, then for all
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
   };
 
   // Tile r of the pipeline. On entry S^T of tile r is in s_cur, K of tile r+1
-  // and V of tile r are in LDS, and the registers hold K of tile r+2 and V of
-  // tile r+1 (loaded during tile r-1). The QK^T products of tile r+1 are
-  // issued before tile r's softmax, so the matrix cores work on them while
+  // and V of tile r are in LDS. The loads of K(r+2) and V(r+1) go into the
+  // stages tile r-1 finished with; the QK^T products of tile r+1 are issued
+  // interleaved with tile r's softmax, so the matrix cores work on them while
   // the vector unit runs the softmax.
-  // S^T accumulators of the current and the next tile; the two swap roles
-  // every tile (the loop is unrolled by two), so they are never copied
   f32x16 s_a[2], s_b[2];
-  auto do_tile = [&](int r, uint16_t* k_this, uint16_t* k_next, uint16_t* v_this,
-                     uint16_t* v_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    __syncthreads();  // tile r-1 done everywhere: k_this and v_next are free
-    if (r + 2 < n_t) store_k(k_this);
-    if (r + 1 < n_t) store_v(v_next);
-    if (r + 3 < n_t) load_k(r + 3);
-    if (r + 2 < n_t) load_v(r + 2);
-    if (!wave_active) return;
-    // block-causal mask, and the missing rows of a partial tile (at most a
-    // few tiles per split; kept out of the common path)
-    const TileLoc L = locate(r);
-    if (__builtin_expect(L.rows < kAttnBlockN || L.abs_base + kAttnBlockN > kmin, 0)) {
-      __asm__ volatile("" ::: "memory");  // keep this block a real branch
-      const int lim = min(L.rows, kend - L.abs_base);  // visible keys of this lane's row
+  auto do_tile = [&](int r, char* k_this, char* k_next, char* v_this, char* v_next,
+                     f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    dma_k(r + 2, k_this);  // past the split's end: empty ranges, nothing read
+    dma_v(r + 1, v_next);
+    if (wave_active) {
+      // block-causal mask, and the missing rows of a partial tile (at most a
+      // few tiles per split; kept out of the common path)
+      const TileLoc L = locate(r);
+      if (__builtin_expect(L.rows < kAttnBlockN || L.abs_base + kAttnBlockN > kmin, 0)) {
+        __asm__ volatile("" ::: "memory");  // keep this block a real branch
+        const int lim = min(L.rows, kend - L.abs_base);  // visible keys of this lane's row
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = kb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
+            s_cur[kb][rr] = key < lim ? s_cur[kb][rr] : kNegInf;
+          }
+      }
+      // online softmax (exp2 domain): row max and the (rare) rescale
+      float mloc = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = kb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
-          s_cur[kb][rr] = key < lim ? s_cur[kb][rr] : kNegInf;
-        }
-    }
-    // online softmax (exp2 domain): row max and the (rare) rescale
-    float mloc = kNegInf;
+        for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s_cur[kb][rr]);
+      const float mt = half_swap_max(mloc) * a.scale_log2;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
+        __asm__ volatile("" ::: "memory");  // keep the rare rescale a real branch
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s_cur[kb][rr]);
-    const float mt = half_swap_max(mloc) * a.scale_log2;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
-      __asm__ volatile("" ::: "memory");  // keep the rare rescale a real branch
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
-#pragma unroll
-      for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    // S^T of tile r+1 on the matrix cores (on a stale stage after the last
-    // tile; unused then) interleaved with tile r's exponentials on the VALU:
-    // MFMA i = (key block i/kDSteps, d-step i%kDSteps) carries softmax
-    // elements kPerMfma*i.. (block 0 of S(t+1) is accumulated while block 0
-    // of S(t) is consumed, so block 1 of S(t+1) can reuse its registers) and
-    // takes its K fragment from an LDS read issued two MFMAs earlier.
-    constexpr int kQK = 2 * T::kDSteps;  // MFMAs of one S^T tile
-    constexpr int kPerMfma = 32 / kQK;   // softmax elements per MFMA
-    const uint16_t* lk = k_next + lrow * T::kKPitch + 8 * half;
-    auto k_frag = [&](int i) {
-      return *reinterpret_cast<const u32x4*>(lk + (i / T::kDSteps) * 32 * T::kKPitch +
-                                             (i % T::kDSteps) * 16);
-    };
-    s_nxt[0] = f32x16{};
-    s_nxt[1] = f32x16{};
-    u32x4 pb[2][2];
-    float pe[32];
-    u32x4 kf[kQK];
-    kf[0] = k_frag(0);
-    kf[1] = k_frag(1);
-#pragma unroll
-    for (int i = 0; i < kQK; ++i) {
-      if (i + 2 < kQK) kf[i + 2] = k_frag(i + 2);
-      s_nxt[i / T::kDSteps] = mfma32x32x16(kf[i], qf[i % T::kDSteps], s_nxt[i / T::kDSteps]);
-#pragma unroll
-      for (int e = kPerMfma * i; e < kPerMfma * (i + 1); ++e)
-        pe[e] = fast_exp2(__builtin_fmaf(s_cur[e >> 4][e & 15], a.scale_log2, -m_use));
-#pragma unroll
-      for (int e = kPerMfma * i; e < kPerMfma * (i + 1); e += 2) {
-        const uint32_t w2 = pack_bf16x2(pe[e], pe[e + 1]);
-        pb[e >> 4][(e >> 3) & 1][(e >> 1) & 3] = w2;
-        l_run = add_bf16x2(w2, l_run);  // the denominator sums the rounded P
+        for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // O^T += V^T P^T, V^T fragments read two MFMAs ahead
-    constexpr int kPV = 4 * T::kDBlocks;
-    const uint16_t* lv = v_this + lrow * T::kVPitch + 8 * half;
-    auto v_frag = [&](int i) {  // i = (db, kb, ks2) with ks2 fastest
-      return *reinterpret_cast<const u32x4*>(lv + (i >> 2) * 32 * T::kVPitch + ((i >> 1) & 1) * 32 +
-                                             (i & 1) * 16);
-    };
-    u32x4 vf[kPV];
-    vf[0] = v_frag(0);
-    vf[1] = v_frag(1);
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      // S^T of tile r+1 (a stale stage after the last tile; unused then)
+      // interleaved with tile r's exponentials: MFMA i = (key block
+      // i/kDSteps, d-step i%kDSteps) carries softmax elements kPerMfma*i..,
+      // with K fragments read two MFMAs ahead.
+      constexpr int kQK = 2 * T::kDSteps;
+      constexpr int kPerMfma = 32 / kQK;
+      s_nxt[0] = f32x16{};
+      s_nxt[1] = f32x16{};
+      u32x4 pb[2][2];
+      float pe[32];
+      u32x4 kf[kQK];
+      kf[0] = k_frag(k_next, 0, 0);
+      kf[1] = k_frag(k_next, 0, 1);
 #pragma unroll
-    for (int i = 0; i < kPV; ++i) {
-      if (i + 2 < kPV) vf[i + 2] = v_frag(i + 2);
-      o[i >> 2] = mfma32x32x16(vf[i], pb[(i >> 1) & 1][i & 1], o[i >> 2]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < kQK; ++i) {
+        if (i + 2 < kQK) kf[i + 2] = k_frag(k_next, (i + 2) / T::kDSteps, (i + 2) % T::kDSteps);
+        s_nxt[i / T::kDSteps] = mfma32x32x16(kf[i], qf[i % T::kDSteps], s_nxt[i / T::kDSteps]);
+#pragma unroll
+        for (int e = kPerMfma * i; e < kPerMfma * (i + 1); ++e)
+          pe[e] = fast_exp2(__builtin_fmaf(s_cur[e >> 4][e & 15], a.scale_log2, -m_use));
+#pragma unroll
+        for (int e = kPerMfma * i; e < kPerMfma * (i + 1); e += 2) {
+          const uint32_t w2 = pack_bf16x2(pe[e], pe[e + 1]);
+          pb[e >> 4][(e >> 3) & 1][(e >> 1) & 3] = w2;
+          l_run = add_bf16x2(w2, l_run);  // the denominator sums the rounded P
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // O^T += V^T P^T, V^T fragments read two MFMAs ahead
+      constexpr int kPV = 4 * T::kDBlocks;
+      u32x4 vf[kPV];
+      vf[0] = v_frag(v_this, 0);
+      vf[1] = v_frag(v_this, 1);
+#pragma unroll
+      for (int i = 0; i < kPV; ++i) {
+        if (i + 2 < kPV) vf[i + 2] = v_frag(v_this, i + 2);
+        o[i >> 2] = mfma32x32x16(vf[i], pb[(i >> 1) & 1][i & 1], o[i >> 2]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    stage_barrier();  // K(r+2), V(r+1) landed; tile r done everywhere
   };
 
   if (n_t > 0) {
-    // prologue: K and V of tile 0 and K of tile 1 into LDS, S^T of tile 0,
-    // then the loads of K(2) and V(1) in flight
-    load_k(0);
-    load_v(0);
-    store_k(kst[0]);
-    store_v(vst[0]);
-    if (n_t > 1) {
-      load_k(1);
-      store_k(kst[1]);
-    }
-    __syncthreads();
+    // prologue: K and V of tile 0 and K of tile 1 into LDS, S^T of tile 0
+    dma_k(0, kst[0]);
+    dma_v(0, vst[0]);
+    dma_k(1, kst[1]);
+    stage_barrier();
     qk(kst[0], s_a);
-    if (n_t > 2) load_k(2);
-    if (n_t > 1) load_v(1);
+    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
   }
   // two tiles per iteration so every stage is fixed at compile time
   for (int r = 0; r < n_t; r += 2) {
