@@ -240,87 +240,144 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     __syncthreads();
   };
 
-  // Tile r of the pipeline. On entry S^T of tile r is in s_cur, K of tile r+1
-  // and V of tile r are in LDS. The loads of K(r+2) and V(r+1) go into the
-  // stages tile r-1 finished with; the QK^T products of tile r+1 are issued
-  // interleaved with tile r's softmax, so the matrix cores work on them while
-  // the vector unit runs the softmax.
+  // block-causal mask and the missing rows of a partial tile r on its scores
+  // (at most a few tiles per split): returns whether tile r needs it
+  auto needs_mask = [&](int r) {
+    const TileLoc L = locate(r);
+    return L.rows < kAttnBlockN || L.abs_base + kAttnBlockN > kmin;
+  };
+  auto apply_mask = [&](int r, f32x16 (&sc)[2]) {
+    const TileLoc L = locate(r);
+    const int lim = min(L.rows, kend - L.abs_base);  // visible keys of this lane's row
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = kb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
+        sc[kb][rr] = key < lim ? sc[kb][rr] : kNegInf;
+      }
+  };
+  auto tile_max = [&](const f32x16 (&sc)[2]) {
+    float m = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, sc[kb][rr]);
+    return m;
+  };
+  // Fold a tile's local max (per lane, before the half-wave exchange) into
+  // the running max; O and l are rescaled only when the max grows by more
+  // than the slack, which is rare after the first tiles.
+  auto update_max = [&](float mloc) {
+    const float mt = half_swap_max(mloc) * a.scale_log2;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
+      __asm__ volatile("" ::: "memory");  // keep the rare rescale a real branch
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+  };
+  // mask (if needed) and max of tile r's scores, then the running max
+  auto prepare = [&](int r, f32x16 (&sc)[2], float mloc) {
+    if (__builtin_expect(needs_mask(r), 0)) {
+      __asm__ volatile("" ::: "memory");  // keep this block a real branch
+      apply_mask(r, sc);
+      mloc = tile_max(sc);
+    }
+    update_max(mloc);
+  };
+
+  // Tile r of the pipeline. On entry the masked S^T of tile r is in s_cur and
+  // the running max covers it; K of tile r+1 and V of tile r are in LDS. The
+  // loads of K(r+2) and V(r+1) go into the stages tile r-1 finished with.
+  // Four blocks of 8 MFMAs keep the vector unit busy beside the matrix cores
+  // (their order is fixed with scheduling barriers):
+  //   1: S^T(r+1) key block 0   || exp of S(r) key block 0 -> P block 0
+  //   2: O^T += V^T P, keys 0-31 || exp of S(r) key block 1 -> P block 1
+  //   3: S^T(r+1) key block 1   || max over S(r+1) key block 0
+  //   4: O^T += V^T P, keys 32-63 || max over S(r+1) key block 1 (second half)
   f32x16 s_a[2], s_b[2];
   auto do_tile = [&](int r, char* k_this, char* k_next, char* v_this, char* v_next,
                      f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     dma_k(r + 2, k_this);  // past the split's end: empty ranges, nothing read
     dma_v(r + 1, v_next);
     if (wave_active) {
-      // block-causal mask, and the missing rows of a partial tile (at most a
-      // few tiles per split; kept out of the common path)
-      const TileLoc L = locate(r);
-      if (__builtin_expect(L.rows < kAttnBlockN || L.abs_base + kAttnBlockN > kmin, 0)) {
-        __asm__ volatile("" ::: "memory");  // keep this block a real branch
-        const int lim = min(L.rows, kend - L.abs_base);  // visible keys of this lane's row
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = kb * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3);
-            s_cur[kb][rr] = key < lim ? s_cur[kb][rr] : kNegInf;
-          }
-      }
-      // online softmax (exp2 domain): row max and the (rare) rescale
-      float mloc = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, s_cur[kb][rr]);
-      const float mt = half_swap_max(mloc) * a.scale_log2;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
-        __asm__ volatile("" ::: "memory");  // keep the rare rescale a real branch
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
       const float m_use = m_run == kNegInf ? 0.f : m_run;
-      // S^T of tile r+1 (a stale stage after the last tile; unused then)
-      // interleaved with tile r's exponentials: MFMA i = (key block
-      // i/kDSteps, d-step i%kDSteps) carries softmax elements kPerMfma*i..,
-      // with K fragments read two MFMAs ahead.
-      constexpr int kQK = 2 * T::kDSteps;
-      constexpr int kPerMfma = 32 / kQK;
-      s_nxt[0] = f32x16{};
-      s_nxt[1] = f32x16{};
+      constexpr int kB = T::kDSteps;  // MFMAs per block (8 at D = 128)
       u32x4 pb[2][2];
-      float pe[32];
-      u32x4 kf[kQK];
-      kf[0] = k_frag(k_next, 0, 0);
-      kf[1] = k_frag(k_next, 0, 1);
+      // exp, bf16 pack and denominator of S(r) elements [e0, e1)
+      auto exp_part = [&](int e0, int e1) {
 #pragma unroll
-      for (int i = 0; i < kQK; ++i) {
-        if (i + 2 < kQK) kf[i + 2] = k_frag(k_next, (i + 2) / T::kDSteps, (i + 2) % T::kDSteps);
-        s_nxt[i / T::kDSteps] = mfma32x32x16(kf[i], qf[i % T::kDSteps], s_nxt[i / T::kDSteps]);
-#pragma unroll
-        for (int e = kPerMfma * i; e < kPerMfma * (i + 1); ++e)
-          pe[e] = fast_exp2(__builtin_fmaf(s_cur[e >> 4][e & 15], a.scale_log2, -m_use));
-#pragma unroll
-        for (int e = kPerMfma * i; e < kPerMfma * (i + 1); e += 2) {
-          const uint32_t w2 = pack_bf16x2(pe[e], pe[e + 1]);
+        for (int e = e0; e < e1; e += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s_cur[e >> 4][e & 15], a.scale_log2, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(s_cur[e >> 4][(e + 1) & 15], a.scale_log2, -m_use));
+          const uint32_t w2 = pack_bf16x2(p0, p1);
           pb[e >> 4][(e >> 3) & 1][(e >> 1) & 3] = w2;
           l_run = add_bf16x2(w2, l_run);  // the denominator sums the rounded P
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // O^T += V^T P^T, V^T fragments read two MFMAs ahead
-      constexpr int kPV = 4 * T::kDBlocks;
-      u32x4 vf[kPV];
-      vf[0] = v_frag(v_this, 0);
-      vf[1] = v_frag(v_this, 1);
+      };
+      // S^T(r+1) key block kb, MFMA i of kB, K fragments two ahead
+      u32x4 kf[2 * kB];
+      auto qk_step = [&](int kb, int i) {
+        if (i == 0) {
+          kf[kb * kB + 0] = k_frag(k_next, kb, 0);
+          kf[kb * kB + 1] = k_frag(k_next, kb, 1);
+        }
+        if (i + 2 < kB) kf[kb * kB + i + 2] = k_frag(k_next, kb, i + 2);
+        s_nxt[kb] = mfma32x32x16(kf[kb * kB + i], qf[i], s_nxt[kb]);
+      };
+      // O^T += V^T P for key block kb, MFMA i of kB = (db, ks2), V^T two ahead
+      u32x4 vf[2 * kB];
+      auto pv_step = [&](int kb, int i) {
+        auto frag = [&](int j) { return v_frag(v_this, (j >> 1) * 4 + kb * 2 + (j & 1)); };
+        if (i == 0) {
+          vf[kb * kB + 0] = frag(0);
+          vf[kb * kB + 1] = frag(1);
+        }
+        if (i + 2 < kB) vf[kb * kB + i + 2] = frag(i + 2);
+        o[i >> 1] = mfma32x32x16(vf[kb * kB + i], pb[kb][i & 1], o[i >> 1]);
+      };
+      constexpr int kEl = 16 / kB;  // exp elements per MFMA in blocks 1-2
+      s_nxt[0] = f32x16{};
+      s_nxt[1] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < kPV; ++i) {
-        if (i + 2 < kPV) vf[i + 2] = v_frag(v_this, i + 2);
-        o[i >> 2] = mfma32x32x16(vf[i], pb[(i >> 1) & 1][i & 1], o[i >> 2]);
+      for (int i = 0; i < kB; ++i) {  // block 1
+        qk_step(0, i);
+        exp_part(kEl * i, kEl * (i + 1));
+        __asm__ volatile("" : "+v"(l_run));
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {  // block 2
+        pv_step(0, i);
+        exp_part(16 + kEl * i, 16 + kEl * (i + 1));
+        __asm__ volatile("" : "+v"(l_run));  // keep the exponentials in this group
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float mloc = kNegInf;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {  // block 3
+        qk_step(1, i);
+#pragma unroll
+        for (int rr = kEl * i; rr < kEl * (i + 1); ++rr) mloc = fmaxf(mloc, s_nxt[0][rr]);
+        __asm__ volatile("" : "+v"(mloc));  // keep the max in this group
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {  // block 4; key block 1 of S(r+1) is read
+        pv_step(1, i);                // once its MFMA chain has had time to finish
+        if (i >= kB / 2) {
+#pragma unroll
+          for (int rr = 2 * kEl * (i - kB / 2); rr < 2 * kEl * (i - kB / 2 + 1); ++rr)
+            mloc = fmaxf(mloc, s_nxt[1][rr]);
+          __asm__ volatile("" : "+v"(mloc));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      prepare(r + 1, s_nxt, mloc);  // (after the last tile: scores unused)
     }
     stage_barrier();  // K(r+2), V(r+1) landed; tile r done everywhere
   };
@@ -332,6 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     dma_k(1, kst[1]);
     stage_barrier();
     qk(kst[0], s_a);
+    if (wave_active) prepare(0, s_a, tile_max(s_a));
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
   }
   // two tiles per iteration so every stage is fixed at compile time
