@@ -31,7 +31,10 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 UNIT_BUDGET_MS = 160.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-ATTN_SOURCE = os.path.join(ROOT, "cached_block_causal_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's sources: counter-derived traffic is reported only
+# while these are unchanged since the counters were taken
+ATTN_SOURCES = [os.path.join(ROOT, "cached_block_causal_amd", "csrc", f)
+                for f in ("attn_fwd.hip", "ws_device.hpp", "ws_launch.hpp")]
 
 
 def parse():
@@ -50,9 +53,12 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def sources_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str):
@@ -63,7 +69,7 @@ def stored_traffic(workload: str):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("attn_source_sha256_16") != source_hash(ATTN_SOURCE):
+    if not rec or rec.get("kernel_sources_sha256_16") != sources_hash(ATTN_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 
