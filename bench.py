@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
+    p.add_argument("--op-bench", action="store_true",
+                   help="instead of the unit step: bandwidth of the cache append (952-token "
+                        "40-head slices) and of the Euler update, one JSON line each")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain copy (the append kernel) of known size, for "
                         "calibrating HBM byte counters")
@@ -134,6 +137,79 @@ def calib_copy(steps: int) -> None:
                       "write_bytes_per_launch": nbytes, "launches": steps}))
 
 
+def op_bench(steps: int) -> None:
+    """HBM bandwidth of ws_kv_append on 952-token x 40-head token-major slices
+    (a v0.2 unit: 32 slice + 920 video tokens) and of ws_fm_euler_step on the
+    whole-performer latent (920 x 40 x 128). Sources and destinations rotate
+    over more than the 256 MB last-level cache, so the bytes come from HBM."""
+    import torch
+
+    from cached_block_causal_amd import KVCache, fm_euler_step, kv_append
+    heads, d, n, nbuf = 40, 128, 952, 24
+    srcs = [(torch.randn(n, heads, d, device="cuda").to(torch.bfloat16),
+             torch.randn(n, heads, d, device="cuda").to(torch.bfloat16)) for _ in range(nbuf)]
+    cache = KVCache(heads, d, n * nbuf)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def appends():
+        cache.rewind(0)
+        for k, v in srcs:
+            kv_append(cache, k, v)
+
+    appends()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        appends()
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) * 1e-3 / (steps * nbuf)
+    nbytes = 2 * (2 * n * heads * d * 2)          # K and V, read + write
+    print(json.dumps({"op": "ws_kv_append", "tokens": n, "heads": heads, "head_dim": d,
+                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
+                      "GB_per_s": round(nbytes / per / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
+    # the same kernel on a 16,384-token slice (670 MB moved per call)
+    big_n = 16384
+    bk = torch.randn(big_n, heads, d, device="cuda").to(torch.bfloat16)
+    bv = torch.randn(big_n, heads, d, device="cuda").to(torch.bfloat16)
+    big = KVCache(heads, d, big_n)
+    big.rewind(0)
+    kv_append(big, bk, bv)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        big.rewind(0)
+        kv_append(big, bk, bv)
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) * 1e-3 / steps
+    nbytes = 2 * (2 * big_n * heads * d * 2)
+    print(json.dumps({"op": "ws_kv_append", "tokens": big_n, "heads": heads, "head_dim": d,
+                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
+                      "GB_per_s": round(nbytes / per / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
+    del bk, bv, big
+    elems = 920 * 40 * 128
+    xs = [torch.randn(elems, device="cuda") for _ in range(nbuf)]
+    vs = [torch.randn(elems, device="cuda").to(torch.bfloat16) for _ in range(nbuf)]
+    for x, v in zip(xs, vs):
+        fm_euler_step(x, v, 0.25)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        for x, v in zip(xs, vs):
+            fm_euler_step(x, v, 0.25)
+    ev1.record()
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) * 1e-3 / (steps * nbuf)
+    nbytes = elems * 10
+    print(json.dumps({"op": "ws_fm_euler_step", "elements": elems,
+                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
+                      "GB_per_s": round(nbytes / per / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -149,6 +225,9 @@ def main():
 
     if args.calib_copy:
         calib_copy(args.steps)
+        return
+    if args.op_bench:
+        op_bench(args.steps)
         return
 
     w = W.BY_NAME[args.workload]

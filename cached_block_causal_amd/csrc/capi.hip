@@ -196,6 +196,9 @@ ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src,
     return fail(WS_ERR_CAPACITY, "len %d + n_tok %d > capacity %d", cache->len, n_tok,
                 cache->capacity);
   if (n_tok == 0) return WS_OK;
+  if ((int64_t)n_tok * (cache->head_dim / 8) > 0x7FFFFFFF || cache->heads > 65535)
+    return fail(WS_ERR_SHAPE, "append of %d tokens x %d heads is too large for one launch", n_tok,
+                cache->heads);
   if (!cache->k || !cache->v || !k_src || !v_src) return fail(WS_ERR_NULL, "a buffer is NULL");
   if (!aligned16(cache->k) || !aligned16(cache->v) || !aligned16(k_src) || !aligned16(v_src))
     return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");

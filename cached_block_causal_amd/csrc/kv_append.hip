@@ -5,48 +5,59 @@
 // its own pre-split cache positions; nothing else moves.)
 //
 // Pure data movement, bound by HBM: 2 * n * heads * D * 2 bytes read and the
-// same written per call (K and V). One thread moves one 16-byte chunk; chunks
-// are numbered with the D/8 chunks of a row fastest, then tokens, then heads,
-// so consecutive lanes write consecutive addresses of a head's cache rows and
-// read whole 128/256-byte rows of the source.
+// same written per call (K and V). One workgroup covers 256 x 4 consecutive
+// 16-byte chunks of one head (the D/8 chunks of a row fastest, then tokens):
+// each thread issues its four loads before its four stores, consecutive lanes
+// write consecutive cache addresses and read whole 128/256-byte rows of the
+// source, and the (token, chunk) split is a shift and a mask.
 #include "ws_device.hpp"
 #include "ws_launch.hpp"
 
 namespace ws {
 
+constexpr int kAppendUnroll = 4;  // 16-byte chunks in flight per thread
+
+// grid: x over the (token, chunk) pairs of one head, y = head, z = K (0) / V (1)
 __global__ __launch_bounds__(256) void kv_append_kernel(
     uint16_t* __restrict__ ck, uint16_t* __restrict__ cv,
     const uint16_t* __restrict__ sk, const uint16_t* __restrict__ sv,
-    int head_dim, int64_t cache_head_stride, int len, int n_tok, int src_heads,
-    int head_begin, int layout, int64_t total_chunks) {
-  // blockIdx.y selects K (0) or V (1): one launch moves both.
-  uint16_t* __restrict__ dst = blockIdx.y == 0 ? ck : cv;
-  const uint16_t* __restrict__ src = blockIdx.y == 0 ? sk : sv;
-  const int cpr = head_dim >> 3;  // 16-byte chunks per row
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += stride) {
-    const int c = (int)(i % cpr);
-    const int64_t rest = i / cpr;
-    const int t = (int)(rest % n_tok);
-    const int h = (int)(rest / n_tok);
-    const int64_t src_row = layout == WS_TOKEN_MAJOR
-                                ? (int64_t)t * src_heads + head_begin + h
-                                : (int64_t)(head_begin + h) * n_tok + t;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + src_row * head_dim + c * 8);
-    *reinterpret_cast<u32x4*>(dst + h * cache_head_stride + (int64_t)(len + t) * head_dim + c * 8) = v;
+    int head_dim, int log2_cpr, int64_t cache_head_stride, int len, int n_tok, int src_heads,
+    int head_begin, int layout) {
+  uint16_t* __restrict__ dst = blockIdx.z == 0 ? ck : cv;
+  const uint16_t* __restrict__ src = blockIdx.z == 0 ? sk : sv;
+  const int h = blockIdx.y;
+  const int per_head = n_tok << log2_cpr;  // 16-byte chunks of this head's rows
+  const int cmask = (1 << log2_cpr) - 1;
+  const int base = blockIdx.x * (256 * kAppendUnroll) + threadIdx.x;
+  const int64_t src_h = layout == WS_TOKEN_MAJOR ? (int64_t)(head_begin + h) * head_dim
+                                                 : (int64_t)(head_begin + h) * n_tok * head_dim;
+  const int64_t src_t = layout == WS_TOKEN_MAJOR ? (int64_t)src_heads * head_dim : head_dim;
+  uint16_t* const dst_h = dst + h * cache_head_stride + (int64_t)len * head_dim;
+  u32x4 v[kAppendUnroll];
+#pragma unroll
+  for (int j = 0; j < kAppendUnroll; ++j) {  // all loads first, then the stores
+    const int i = base + j * 256;
+    if (i < per_head)
+      v[j] = *reinterpret_cast<const u32x4*>(src + src_h + (int64_t)(i >> log2_cpr) * src_t +
+                                             (i & cmask) * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < kAppendUnroll; ++j) {
+    const int i = base + j * 256;
+    if (i < per_head)
+      *reinterpret_cast<u32x4*>(dst_h + (int64_t)(i >> log2_cpr) * head_dim + (i & cmask) * 8) = v[j];
   }
 }
 
 hipError_t launch_kv_append(uint16_t* ck, uint16_t* cv, const uint16_t* sk, const uint16_t* sv,
                             int heads, int head_dim, int capacity, int len, int n_tok,
                             int src_heads, int head_begin, int layout, hipStream_t stream) {
-  const int64_t total = (int64_t)heads * n_tok * (head_dim / 8);
-  const int threads = 256;
-  int64_t blocks = (total + threads - 1) / threads;
-  if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 blocks per CU
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks, 2), dim3(threads), 0, stream,
-                     ck, cv, sk, sv, head_dim, (int64_t)capacity * head_dim, len, n_tok,
-                     src_heads, head_begin, layout, total);
+  const int log2_cpr = head_dim == 128 ? 4 : 3;
+  const int64_t per_head = (int64_t)n_tok << log2_cpr;
+  const unsigned bx = (unsigned)((per_head + 256 * kAppendUnroll - 1) / (256 * kAppendUnroll));
+  hipLaunchKernelGGL(kv_append_kernel, dim3(bx, heads, 2), dim3(256), 0, stream, ck, cv, sk, sv,
+                     head_dim, log2_cpr, (int64_t)capacity * head_dim, len, n_tok, src_heads,
+                     head_begin, layout);
   return hipGetLastError();
 }
 
