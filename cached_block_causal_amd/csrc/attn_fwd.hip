@@ -24,7 +24,10 @@
 //    4 keys of one dimension.
 //  * Online softmax in the exp2 domain, fp32, with the running max allowed to
 //    lag the true max by up to 2^8 before O and l are rescaled (rescales are
-//    rare once the max settles; the result is the same up to rounding).
+//    rare once the max settles; the result is the same up to rounding). The
+//    scale times log2 e is folded into Q once (rounded back to bf16) and
+//    every S^T chain starts from the accumulator -max, so the MFMAs hand the
+//    exponent arguments straight to v_exp_f32.
 //  * Software pipeline over 64-key tiles: while the vector unit runs the
 //    softmax of tile t, the matrix cores compute S^T of tile t+1 (their order
 //    is fixed with scheduling barriers), then O^T += V^T P^T of tile t. K and
@@ -152,12 +155,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     // wait for Q here, once: otherwise paths that skip the prologue leave the
     // loads pending and every tile's first MFMA would wait on all loads
     __builtin_amdgcn_s_waitcnt(0);
+    // fold the softmax scale (times log2 e) into Q, rounded back to bf16: the
+    // MFMAs then produce scores in log2 units and the softmax needs no
+    // multiply (one more bf16 rounding of each q element, within the
+    // tolerance of the result)
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        qf[ks][w] = pack_bf16x2(bf16_lo(qf[ks][w]) * a.scale_log2, bf16_hi(qf[ks][w]) * a.scale_log2);
   }
 
   f32x16 o[T::kDBlocks];
 #pragma unroll
   for (int db = 0; db < T::kDBlocks; ++db) o[db] = f32x16{};
   float m_run = kNegInf;  // running max of scaled scores (log2 units)
+  // Scores are produced already shifted by m_off (m_run once that is
+  // finite, else 0): every S^T chain starts from the accumulator -m_off.
+  float m_off = 0.f;
+  f32x16 neg_off = f32x16{};
   float l_run = 0.f;      // this lane's share of the softmax denominator
 
   // ---- LDS layout: byte (G, row, slot) = G * kGroupBytes + row * 64 + slot * 16
@@ -227,12 +243,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   };
   // S^T of one 64-key tile from an LDS K stage
   auto qk = [&](const char* kstage, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < T::kDSteps; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(k_frag(kstage, kb, ks), qf[ks], s[kb]);
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32x32x16(k_frag(kstage, kb, ks), qf[ks], ks == 0 ? neg_off : s[kb]);
   };
   // the tile's global loads into LDS are complete for this wave, then for all
   auto stage_barrier = [&]() {
@@ -265,11 +280,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
       for (int rr = 0; rr < 16; ++rr) m = fmaxf(m, sc[kb][rr]);
     return m;
   };
-  // Fold a tile's local max (per lane, before the half-wave exchange) into
-  // the running max; O and l are rescaled only when the max grows by more
-  // than the slack, which is rare after the first tiles.
-  auto update_max = [&](float mloc) {
-    const float mt = half_swap_max(mloc) * a.scale_log2;
+  // Fold a tile's local max (per lane, before the half-wave exchange, of the
+  // shifted scores sc) into the running max. O and l are rescaled only when
+  // the max grows by more than the slack, which is rare after the first
+  // tiles; the offset then moves to the new max, sc with it.
+  auto update_max = [&](f32x16 (&sc)[2], float mloc) {
+    const float mt = half_swap_max(mloc) + m_off;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
       __asm__ volatile("" ::: "memory");  // keep the rare rescale a real branch
       const float m_new = fmaxf(m_run, mt);
@@ -278,6 +294,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
       for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      const float off_new = m_new == kNegInf ? 0.f : m_new;
+      const float shift = m_off - off_new;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sc[kb] += shift;
+      m_off = off_new;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) neg_off[rr] = -off_new;
     }
   };
   // mask (if needed) and max of tile r's scores, then the running max
@@ -287,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
       apply_mask(r, sc);
       mloc = tile_max(sc);
     }
-    update_max(mloc);
+    update_max(sc, mloc);
   };
 
   // Tile r of the pipeline. On entry the masked S^T of tile r is in s_cur and
@@ -305,19 +328,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     dma_k(r + 2, k_this);  // past the split's end: empty ranges, nothing read
     dma_v(r + 1, v_next);
     if (wave_active) {
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
       constexpr int kB = T::kDSteps;  // MFMAs per block (8 at D = 128)
       u32x4 pb[2][2];
-      // exp, bf16 pack and denominator of S(r) elements [e0, e1)
-      auto exp_part = [&](int e0, int e1) {
-#pragma unroll
-        for (int e = e0; e < e1; e += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s_cur[e >> 4][e & 15], a.scale_log2, -m_use));
-          const float p1 = fast_exp2(__builtin_fmaf(s_cur[e >> 4][(e + 1) & 15], a.scale_log2, -m_use));
-          const uint32_t w2 = pack_bf16x2(p0, p1);
-          pb[e >> 4][(e >> 3) & 1][(e >> 1) & 3] = w2;
-          l_run = add_bf16x2(w2, l_run);  // the denominator sums the rounded P
-        }
+      // Softmax of S(r) (scores already scaled and shifted), pipelined over
+      // the 16 MFMA slots of blocks 1-2 (pair j = elements 2j, 2j+1 of the
+      // lane's 32 scores): slot j exponentiates pair j and packs pair j-1 to
+      // bf16 (adding it to the denominator), so no vector instruction of a
+      // slot waits for another one of the same slot.
+      float ex[32];
+      auto exp_pair = [&](int j) {
+        ex[2 * j] = fast_exp2(s_cur[j >> 3][(2 * j) & 15]);
+        ex[2 * j + 1] = fast_exp2(s_cur[j >> 3][(2 * j + 1) & 15]);
+      };
+      auto pack_pair = [&](int j) {
+        const uint32_t w2 = pack_bf16x2(ex[2 * j], ex[2 * j + 1]);
+        pb[j >> 3][(j >> 2) & 1][j & 3] = w2;
+        l_run = add_bf16x2(w2, l_run);  // the denominator sums the rounded P
+      };
+      // slot j's share; the empty asm keeps each result in its slot
+      auto softmax_slot = [&](int j) {
+        if (j < 16) exp_pair(j);
+        if (j >= 1) pack_pair(j - 1);
+        if (j < 16) __asm__ volatile("" : "+v"(ex[2 * j]), "+v"(ex[2 * j + 1]));
+        __asm__ volatile("" : "+v"(l_run));
       };
       // S^T(r+1) key block kb, MFMA i of kB, K fragments two ahead
       u32x4 kf[2 * kB];
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
           kf[kb * kB + 1] = k_frag(k_next, kb, 1);
         }
         if (i + 2 < kB) kf[kb * kB + i + 2] = k_frag(k_next, kb, i + 2);
-        s_nxt[kb] = mfma32x32x16(kf[kb * kB + i], qf[i], s_nxt[kb]);
+        s_nxt[kb] = mfma32x32x16(kf[kb * kB + i], qf[i], i == 0 ? neg_off : s_nxt[kb]);
       };
       // O^T += V^T P for key block kb, MFMA i of kB = (db, ks2), V^T two ahead
       u32x4 vf[2 * kB];
@@ -340,27 +373,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
         if (i + 2 < kB) vf[kb * kB + i + 2] = frag(i + 2);
         o[i >> 1] = mfma32x32x16(vf[kb * kB + i], pb[kb][i & 1], o[i >> 1]);
       };
-      constexpr int kEl = 16 / kB;  // exp elements per MFMA in blocks 1-2
-      s_nxt[0] = f32x16{};
-      s_nxt[1] = f32x16{};
+      constexpr int kEl = 16 / kB;  // max elements per MFMA in blocks 3-4
+      constexpr int kPp = 8 / kB;   // softmax pairs per MFMA in blocks 1-2
 #pragma unroll
       for (int i = 0; i < kB; ++i) {  // block 1
         qk_step(0, i);
-        exp_part(kEl * i, kEl * (i + 1));
-        __asm__ volatile("" : "+v"(l_run));
+#pragma unroll
+        for (int j = kPp * i; j < kPp * (i + 1); ++j) softmax_slot(j);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < kB; ++i) {  // block 2
         pv_step(0, i);
-        exp_part(16 + kEl * i, 16 + kEl * (i + 1));
-        __asm__ volatile("" : "+v"(l_run));  // keep the exponentials in this group
+#pragma unroll
+        for (int j = 8 + kPp * i; j < 8 + kPp * (i + 1); ++j) softmax_slot(j);
         __builtin_amdgcn_sched_barrier(0);
       }
       float mloc = kNegInf;
 #pragma unroll
       for (int i = 0; i < kB; ++i) {  // block 3
         qk_step(1, i);
+        if (i == 0) softmax_slot(16);  // the last pack
 #pragma unroll
         for (int rr = kEl * i; rr < kEl * (i + 1); ++rr) mloc = fmaxf(mloc, s_nxt[0][rr]);
         __asm__ volatile("" : "+v"(mloc));  // keep the max in this group
