@@ -12,8 +12,12 @@ step is the same workload. All inputs are resident in HBM before timing.
 
 Prints one JSON line. `value` is attention TFLOP/s over the whole unit (all
 denoise steps' algorithmic attention FLOPs / wall time of the unit);
-`roofline` is the split-KV attention kernel against the bf16 MFMA peak, its
-duration measured with HIP events around each launch on the launch stream.
+`roofline` is the split-KV attention kernel against the bf16 MFMA peak (or,
+for a workload below the ridge point, against HBM bandwidth), its duration
+measured with HIP events around each launch on the launch stream.
+
+`--workload v02_history_prefill` measures the multi-unit form instead: one
+step is one block-causal call over all 64 cached units (partial + merge).
 """
 from __future__ import annotations
 
@@ -117,6 +121,122 @@ def cpu_baseline(w, budget_s: float):
             "sample": f"fp64 NumPy oracle on {done} of {w.steps * w.heads} (denoise step, head) "
                       f"attention problems of this workload ({w.n_q} queries x {w.n_keys} keys "
                       f"each), {elapsed:.2f} s of compute; host has {os.cpu_count()} logical CPUs"}
+
+
+def roofline(w, attn_avg_ms: float, attn_min_ms: float) -> dict:
+    """The attention kernel against the roofline that bounds it: the bf16
+    MFMA peak above the ridge point (peak FLOP/s / peak B/s), HBM below it.
+    Both fractions are given."""
+    flops, kv = w.attn_flops(), w.attn_kv_bytes()
+    tf = flops / (attn_avg_ms * 1e-3) / 1e12
+    gbs = kv / (attn_avg_ms * 1e-3) / 1e9
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm = flops / kv < ridge
+    r = {"kernel": "attn_partial_kernel<%d>" % w.head_dim, "bound": "hbm" if hbm else "mfma",
+         "achieved": round(gbs if hbm else tf, 2), "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
+         "unit": "GB/s" if hbm else "TFLOP/s",
+         "frac": round((gbs / PEAK_HBM_GBS) if hbm else (tf / PEAK_BF16_TFLOPS), 4),
+         "traffic": stored_traffic(w.name),
+         "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+         "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+         "launch_ms_avg": round(attn_avg_ms, 5), "launch_ms_min": round(attn_min_ms, 5)}
+    return r
+
+
+def cpu_baseline_prefill(w, budget_s: float):
+    """The fp64 oracle on (head, unit) problems of the multi-unit call: the
+    queries of one unit over the cache up to that unit's end, the largest
+    units first, until about budget_s seconds of CPU time."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import gen as G
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count() or 1
+    ids = G.history_unit_ids(w)
+    kend = w.unit_kend()
+    done, flops, elapsed = 0, 0, 0.0
+    head = [w.head_begin]
+    hk, hv = G.history_bits(w, head)
+    for u in reversed(range(w.cached_units)):
+        q = G.prefill_queries(w, head, units=[u])
+        t0 = time.perf_counter()
+        O.attention(q, hk[:, :kend[u]], hv[:, :kend[u]], np.full(w.video_tokens, u), ids[:kend[u]],
+                    1 / np.sqrt(w.head_dim))
+        elapsed += time.perf_counter() - t0
+        done += 1
+        flops += 4 * w.head_dim * w.video_tokens * kend[u]
+        if elapsed >= budget_s:
+            break
+    return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on {done} of {w.cached_units * w.heads} (head, unit) "
+                      f"problems of this call (one unit's {w.video_tokens} queries over the cache "
+                      f"up to its end, largest first), {elapsed:.2f} s of compute; host has "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def prefill_bench(w, args) -> None:
+    """One step = one multi-unit block-causal call (ws_attn_partial +
+    ws_attn_merge) over the whole cached history."""
+    import torch
+
+    from cached_block_causal_amd import AttnCall, KVCache, kv_append
+    from workloads import gen as G
+    from workloads.device import dev_bits
+    heads = list(range(w.head_begin, w.head_begin + w.heads))
+    t_setup = time.perf_counter()
+    cache = KVCache(w.heads, w.head_dim, w.capacity)
+    for u in range(w.cached_units):                      # history (untimed)
+        k, v = G.cache_unit_tokens(w, u, heads)
+        kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
+    q = dev_bits(G.prefill_queries(w))
+    call = AttnCall(cache, q, q_unit_begin=w.q_unit_begin(), unit_kend=w.unit_kend(),
+                    n_splits=args.splits)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    for _ in range(args.warmup):
+        call.partial()
+        call.merge()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for a, b in ev:
+        a.record()
+        call.partial()
+        b.record()
+        call.merge()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    out = {
+        "metric": "attention TFLOP/s of one multi-unit block-causal call (visible query-key "
+                  "pairs only), with % of bf16 MFMA peak",
+        "value": round(w.attn_flops() / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) Q/K/V)",
+        "config": {"workload": w.name, "heads": w.heads, "heads_total": w.heads_total,
+                   "head_dim": w.head_dim, "n_q": w.n_q, "n_keys": w.n_keys,
+                   "units": w.cached_units, "visible_pairs_per_head": w.visible_pairs(),
+                   "splits": call.splits},
+        "roofline": roofline(w, sum(attn_ms) / len(attn_ms), min(attn_ms)),
+        "host_wall_s": round(wall, 3),
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
 
 
 def calib_copy(steps: int) -> None:
@@ -231,6 +351,9 @@ def main():
         return
 
     w = W.BY_NAME[args.workload]
+    if w.prefill:
+        prefill_bench(w, args)
+        return
     heads = list(range(w.head_begin, w.head_begin + w.heads))
     t_setup = time.perf_counter()
     cache = KVCache(w.heads, w.head_dim, w.capacity)
@@ -290,8 +413,6 @@ def main():
 
     flops_step = w.attn_flops()
     value = flops_step * w.steps / (ms_per_step * 1e-3) / 1e12
-    achieved = flops_step / (attn_avg_ms * 1e-3) / 1e12
-    traffic = stored_traffic(w.name)
     out = {
         "metric": "attention TFLOP/s per 160 ms unit (4 denoise steps), with % of bf16 MFMA "
                   "peak per denoise step and us/unit vs the 160 ms budget",
@@ -310,12 +431,7 @@ def main():
                    "head_dim": w.head_dim, "n_q": w.n_q, "cache_len": w.cache_len,
                    "n_keys": w.n_keys, "denoise_steps": w.steps, "splits": splits,
                    "slice_tokens": w.slice_tokens, "commit_tokens": w.n_self},
-        "roofline": {"kernel": "attn_partial_kernel<%d>" % w.head_dim, "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
-                     "launch_ms_avg": round(attn_avg_ms, 5),
-                     "launch_ms_min": round(min(attn_ms), 5)},
+        "roofline": roofline(w, attn_avg_ms, min(attn_ms)),
         "us_per_unit": round(ms_per_step * 1e3, 1),
         "unit_budget_frac": round(ms_per_step / UNIT_BUDGET_MS, 5),
         "attention_layers_per_unit_budget": int(UNIT_BUDGET_MS // ms_per_step),

@@ -40,7 +40,11 @@
 //  * Work items (head, split, query tile) are ordered with the query tile
 //    fastest and mapped onto blockIdx so that the items of one (head, split)
 //    land on the same XCD (workgroups are dispatched round-robin over the 8
-//    XCDs): the K/V chunk they share is then served from that XCD's L2.
+//    XCDs): the K/V chunk they share is then served from that XCD's L2. The
+//    query tiles go last to first, so that in a call spanning many units
+//    (a block triangle of work) the tiles with the most keys start first.
+//    Tiles past a query tile's last visible key are never loaded, and the
+//    mask is applied only to tiles that reach past its first row's keys.
 //  * Rows past the visible range read as zeros and are masked to -inf, so
 //    unused cache capacity never reaches the arithmetic.
 #include <math.h>
@@ -110,7 +114,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   const int per_xcd = gridDim.x >> 3;
   const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (w >= a.n_items) return;
-  const int qt = w % a.n_qtiles;
+  // query tiles in decreasing order: with several units in one call the
+  // later tiles see more keys, so the longest items are dispatched first
+  const int qt = a.n_qtiles - 1 - w % a.n_qtiles;
   const int hs = w / a.n_qtiles;
   const int split = hs % a.n_splits;
   const int h = hs / a.n_splits;

@@ -30,17 +30,25 @@ def poisoned_cache(heads, head_dim, capacity):
 
 def fill_history(cache, w, slice_heads_all=True):
     """Append the workload's prior units (head-major commits of this GPU's
-    heads) and then the current unit's slice (token-major, all w.heads_total
-    heads, keeping this GPU's block) through ws_kv_append."""
+    heads) and then, for the streaming step, the current unit's slice
+    (token-major, all w.heads_total heads, keeping this GPU's block) through
+    ws_kv_append."""
     from cached_block_causal_amd import kv_append
     heads = list(range(w.head_begin, w.head_begin + w.heads))
     for u in range(w.cached_units):
         k, v = G.cache_unit_tokens(w, u, heads)
         kv_append(cache, dev_bits(k), dev_bits(v), head_begin=0, layout="head")
+    if w.prefill:
+        return
     src_heads = range(w.heads_total) if slice_heads_all else heads
     k, v = G.cache_unit_tokens(w, w.current_unit, src_heads, w.slice_tokens)
     kv_append(cache, dev_bits(G.token_major(k)), dev_bits(G.token_major(v)),
               head_begin=w.head_begin if slice_heads_all else 0, layout="token")
+
+
+def all_finite_bits(bits) -> bool:
+    """No bf16 NaN or infinity (exponent field all ones) among the bits."""
+    return not np.any((np.asarray(bits, dtype=np.uint16) & 0x7F80) == 0x7F80)
 
 
 def errors(got_bits: np.ndarray, want: np.ndarray):

@@ -40,12 +40,31 @@ def test_streams_are_deterministic_and_per_head():
 
 def test_workload_key_counts():
     want = {"tiny": 804, "v01_unit": 9372, "v02_rank_share": 61880,
-            "v02_whole_performer": 61880, "audio_long_history": 244772}
+            "v02_whole_performer": 61880, "audio_long_history": 244772,
+            "v02_history_prefill": 60928}
     for w in W.ALL:
         assert w.n_keys == want[w.name]
     assert W.TINY.cache_len == 552 and W.V02_RANK.cache_len == 60960
     assert W.AUDIO_LONG.cache_len == 244768
     assert W.V02_RANK.latent_elems == 920 * 10 * 128
+
+
+def test_prefill_unit_table():
+    """The multi-unit form: unit u's 920 queries see the cache up to the end
+    of unit u (952 tokens per unit), so the visible pairs are a block
+    triangle; the streaming form is one unit seeing every key."""
+    w = W.V02_PREFILL
+    qb, ke = w.q_unit_begin(), w.unit_kend()
+    assert len(qb) == 65 and qb[0] == 0 and qb[-1] == w.n_q == 58880
+    assert ke[0] == 952 and ke[-1] == w.n_keys == w.cache_len == 60928
+    assert w.visible_pairs() == 920 * 952 * (64 * 65 // 2)
+    assert W.V02_RANK.visible_pairs() == 920 * 61880
+    assert W.V02_RANK.q_unit_begin() == [0, 920] and W.V02_RANK.unit_kend() == [61880]
+    ids = G.history_unit_ids(w)
+    assert ids.shape == (60928,) and ids[-1] == 63
+    q = G.prefill_queries(w, heads=[3], units=[0, 5])
+    assert q.shape == (1, 1840, 128)
+    assert np.array_equal(q[:, 920:], G.bf16_heads(w.seed, G.TAG_Q, 5, 0, [3], 920, 128))
 
 
 def test_history_matches_unit_by_unit_construction():

@@ -26,7 +26,8 @@ class Workload:
     slice_tokens: int       # thinker K/V slice tokens per unit
     audio_tokens: int       # latent audio tokens per unit
     cached_units: int       # complete prior units in the cache
-    query: str              # "video" or "audio": which latent is denoised
+    query: str              # "video" or "audio": which latent is denoised;
+                            # "prefill": every cached unit's video tokens at once
     history_audio: bool     # history units also hold their audio tokens
     data_scale: float = 1.0  # Q/K/V ~ N(0,1) * data_scale before bf16 rounding
     steps: int = 4          # denoise steps per unit
@@ -43,22 +44,43 @@ class Workload:
                 + (self.audio_tokens if self.history_audio else 0))
 
     @property
+    def prefill(self) -> bool:
+        """Multi-unit form: the queries of all cached units in one call, each
+        unit seeing the cache up to its own end (no current unit)."""
+        return self.query == "prefill"
+
+    @property
     def history_len(self) -> int:
         return self.cached_units * self.unit_tokens
 
     @property
     def cache_len(self) -> int:
         """Valid cache rows at attention time: history + current slice."""
-        return self.history_len + self.slice_tokens
+        return self.history_len + (0 if self.prefill else self.slice_tokens)
 
     @property
     def n_q(self) -> int:
+        if self.prefill:
+            return self.cached_units * self.video_tokens
         return self.video_tokens if self.query == "video" else self.audio_tokens
 
     @property
     def n_self(self) -> int:
         """The current unit's own latent tokens of the denoised modality."""
-        return self.n_q
+        return 0 if self.prefill else self.n_q
+
+    def q_unit_begin(self) -> list:
+        """First query row of every unit, then n_q (the call's unit table)."""
+        if not self.prefill:
+            return [0, self.n_q]
+        return [u * self.video_tokens for u in range(self.cached_units + 1)]
+
+    def unit_kend(self) -> list:
+        """Keys visible to each unit of the call: a unit sees the cache up to
+        its own end (streaming: everything, its own tokens included)."""
+        if not self.prefill:
+            return [self.n_keys]
+        return [(u + 1) * self.unit_tokens for u in range(self.cached_units)]
 
     @property
     def n_keys(self) -> int:
@@ -79,10 +101,15 @@ class Workload:
         the current slice and the current unit's committed latents."""
         return self.history_len + self.unit_tokens
 
+    def visible_pairs(self) -> int:
+        """(query, key) pairs one head's call computes (masked pairs excluded)."""
+        qb, ke = self.q_unit_begin(), self.unit_kend()
+        return sum((qb[u + 1] - qb[u]) * ke[u] for u in range(len(ke)))
+
     def attn_flops(self) -> int:
-        """Algorithmic attention FLOPs of one denoise step (streaming form):
-        4*D per visible (query, key) pair per head (QK^T and PV)."""
-        return 4 * self.head_dim * self.n_q * self.n_keys * self.heads
+        """Algorithmic attention FLOPs of one call: 4*D per visible (query,
+        key) pair per head (QK^T and PV)."""
+        return 4 * self.head_dim * self.visible_pairs() * self.heads
 
     def attn_kv_bytes(self) -> int:
         """K and V bytes of one denoise step, each visible key read once."""
@@ -132,5 +159,16 @@ AUDIO_LONG = Workload(
     video_tokens=920, slice_tokens=32, audio_tokens=4, cached_units=256,
     query="audio", history_audio=True)
 
-ALL = [TINY, V01_UNIT, V02_RANK, V02_WHOLE, AUDIO_LONG]
+V02_PREFILL = Workload(
+    name="v02_history_prefill",
+    description="multi-unit block-causal attention at scale: re-encode the v0.2 rank "
+                "share's 64-unit history in one call, the 920 video tokens of every "
+                "unit as queries over the cache up to that unit's end (58,880 queries, "
+                "60,928 keys, 10 heads, head_dim 128)",
+    heads_total=40, heads=10, head_begin=0, head_dim=128,
+    video_tokens=920, slice_tokens=32, audio_tokens=0, cached_units=64,
+    query="prefill", history_audio=False, steps=1)
+
+ALL = [TINY, V01_UNIT, V02_RANK, V02_WHOLE, AUDIO_LONG, V02_PREFILL]
+STREAMING = [w for w in ALL if not w.prefill]   # the per-unit denoising step
 BY_NAME = {w.name: w for w in ALL}

@@ -138,6 +138,8 @@ def history_unit_ids(w: Workload) -> np.ndarray:
     """Unit id of every valid cache row at attention time (construction log):
     prior units 0..U-1 in order, then the current unit's slice (unit U)."""
     ids = np.repeat(np.arange(w.cached_units, dtype=np.int64), w.unit_tokens)
+    if w.prefill:
+        return ids
     return np.concatenate([ids, np.full(w.slice_tokens, w.current_unit, dtype=np.int64)])
 
 
@@ -156,7 +158,18 @@ def history_bits(w: Workload, heads=None):
         k[:, pos:pos + w.unit_tokens] = ku
         v[:, pos:pos + w.unit_tokens] = vu
         pos += w.unit_tokens
-    ku, vu = cache_unit_tokens(w, w.current_unit, heads, w.slice_tokens)
-    k[:, pos:] = ku
-    v[:, pos:] = vu
+    if not w.prefill:
+        ku, vu = cache_unit_tokens(w, w.current_unit, heads, w.slice_tokens)
+        k[:, pos:] = ku
+        v[:, pos:] = vu
     return k, v
+
+
+def prefill_queries(w: Workload, heads=None, units=None) -> np.ndarray:
+    """Queries of the multi-unit form: the video tokens of every cached unit
+    (or of `units`), unit by unit, head-major bf16 bits [len(heads)][n][D]."""
+    if heads is None:
+        heads = range(w.head_begin, w.head_begin + w.heads)
+    units = range(w.cached_units) if units is None else units
+    return np.concatenate([bf16_heads(w.seed, TAG_Q, u, 0, heads, w.video_tokens, w.head_dim,
+                                      w.data_scale) for u in units], axis=1)
