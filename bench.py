@@ -18,6 +18,9 @@ measured with HIP events around each launch on the launch stream.
 
 `--workload v02_history_prefill` measures the multi-unit form instead: one
 step is one block-causal call over all 64 cached units (partial + merge).
+`--workload joint_rank_share` runs the unit with the audio and video queries
+in one call per denoise step, and also times the same unit with one call per
+modality (`separate`).
 """
 from __future__ import annotations
 
@@ -107,10 +110,14 @@ def cpu_baseline(w, budget_s: float):
             q, ks, vs, _ = G.step_tensors(w, step, heads=head)
             t0 = time.perf_counter()
             k, v, ku = O.streaming_keys(hk, hv, w.cache_len, ids, ks, vs, w.current_unit)
-            O.attention(q, k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(w.head_dim))
+            qu = np.full(w.n_q, w.current_unit)
+            if w.joint:   # audio rows and keys first; video queries also see the audio tokens
+                ku[w.cache_len + w.audio_tokens:] += 1
+                qu[w.audio_tokens:] += 1
+            O.attention(q, k, v, qu, ku, 1 / np.sqrt(w.head_dim))
             elapsed += time.perf_counter() - t0
             done += 1
-            flops += 4 * w.head_dim * w.n_q * w.n_keys
+            flops += 4 * w.head_dim * w.visible_pairs()
             if elapsed >= budget_s:
                 break
         if elapsed >= budget_s:
@@ -370,11 +377,23 @@ def main():
     dvs = [dev_bits(t[2]) for t in steps_in]
     dvel = [dev_bits(t[3]) for t in steps_in]
     x = torch.from_numpy(G.x0(w)).to("cuda")
-    calls = [AttnCall(cache, dq[0], dks[0], dvs[0], n_splits=args.splits)]
-    calls += [AttnCall(cache, dq[s], dks[s], dvs[s], n_splits=args.splits,
+    qb, ke = w.q_unit_begin(), w.unit_kend()
+    calls = [AttnCall(cache, dq[0], dks[0], dvs[0], qb, ke, n_splits=args.splits)]
+    calls += [AttnCall(cache, dq[s], dks[s], dvs[s], qb, ke, n_splits=args.splits,
                        workspace=calls[0].workspace)      # one workspace for all steps
               for s in range(1, w.steps)]
     splits = calls[0].splits
+    sep_calls = None
+    if w.joint:
+        # the same unit with one call per modality (audio rows first)
+        a = w.audio_tokens
+
+        def part(t, lo, hi):
+            return t[:, lo:hi].contiguous()
+
+        sep_calls = [[AttnCall(cache, part(dq[s], 0, a), part(dks[s], 0, a), part(dvs[s], 0, a)),
+                      AttnCall(cache, part(dq[s], a, w.n_q), part(dks[s], a, w.n_q),
+                               part(dvs[s], a, w.n_q))] for s in range(w.steps)]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -382,16 +401,19 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_attn)]
 
-    def unit_step(timed_events=None):
+    def unit_step(timed_events=None, per_step=None):
         cache.rewind(history_len)
         kv_append(cache, slice_k, slice_v, head_begin=w.head_begin)
         for s in range(w.steps):
+            step_calls = [calls[s]] if per_step is None else per_step[s]
             if timed_events is not None:
                 timed_events[s][0].record()
-            calls[s].partial()
+            for c in step_calls:
+                c.partial()
             if timed_events is not None:
                 timed_events[s][1].record()
-            calls[s].merge()
+            for c in step_calls:
+                c.merge()
             fm_euler_step(x, dvel[s], w.dt)
         kv_append(cache, dks[-1], dvs[-1], layout="head")   # commit the unit's latents
 
@@ -438,6 +460,23 @@ def main():
         "host_wall_s": round(wall, 3),
         "setup_s": round(setup_s, 2),
     }
+    if sep_calls is not None:
+        # the same unit, one call per modality per denoise step
+        for _ in range(args.warmup):
+            unit_step(per_step=sep_calls)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            unit_step(ev[i * w.steps:(i + 1) * w.steps], per_step=sep_calls)
+        t1.record()
+        torch.cuda.synchronize()
+        sep_ms = t0.elapsed_time(t1) / args.steps
+        sep_attn = [a.elapsed_time(b) for a, b in ev]
+        out["separate"] = {"ms_per_step": round(sep_ms, 4),
+                           "attention_ms_avg": round(sum(sep_attn) / len(sep_attn), 5),
+                           "splits": [c.splits for c in sep_calls[0]],
+                           "what": "one call for the audio and one for the video queries per "
+                                   "denoise step, attention time = both partial launches"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

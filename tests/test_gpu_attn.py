@@ -75,6 +75,39 @@ def test_audio_long_history_sampled_heads():
     _streaming_case(W.AUDIO_LONG, [0, 3], heads_sampled=[0, 13, 39])
 
 
+@pytest.mark.timeout(600)
+def test_joint_audio_video_call_sampled_heads():
+    """The unit's audio and video queries in one call (audio rows first): on
+    sampled heads every row equals the oracle, where the audio rows see the
+    cache and the unit's audio tokens and the video rows also the unit's
+    video tokens; the audio rows also agree with a call for audio alone."""
+    need_gpu()
+    from cached_block_causal_amd import AttnCall
+    w = W.JOINT_RANK
+    print(f"joint {w.name} n_q {w.n_q} n_keys {w.n_keys}", flush=True)
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    assert cache.len == w.cache_len
+    q, ks, vs, _ = G.step_tensors(w, 1)
+    out = host_bits(AttnCall(cache, dev_bits(q), dev_bits(ks), dev_bits(vs), w.q_unit_begin(),
+                             w.unit_kend()).run())
+    a = w.audio_tokens
+    alone = host_bits(AttnCall(cache, dev_bits(q[:, :a].copy()), dev_bits(ks[:, :a].copy()),
+                               dev_bits(vs[:, :a].copy())).run())
+    sel = [0, 9]
+    hk, hv = G.history_bits(w, [w.head_begin + h for h in sel])
+    ids = G.history_unit_ids(w)
+    u = w.current_unit
+    k = np.concatenate([O.bf16_to_f64(hk), O.bf16_to_f64(ks[sel])], axis=1)
+    v = np.concatenate([O.bf16_to_f64(hv), O.bf16_to_f64(vs[sel])], axis=1)
+    ku = np.concatenate([ids, np.full(a, u), np.full(w.video_tokens, u + 1)])
+    qu = np.concatenate([np.full(a, u), np.full(w.video_tokens, u + 1)])
+    want = O.attention(q[sel], k, v, qu, ku, 1 / np.sqrt(w.head_dim))
+    print(assert_close(out[sel], want, "joint call"), flush=True)
+    assert_close(alone[sel], want[:, :a], "audio alone")
+    assert_close(out[sel][:, :a], want[:, :a], "joint audio rows")
+
+
 def _multi_unit_tiny():
     """The tiny workload in its multi-unit form: all three units' tokens in
     the cache, queries of all three units, unit u seeing units <= u."""

@@ -41,12 +41,26 @@ def test_streams_are_deterministic_and_per_head():
 def test_workload_key_counts():
     want = {"tiny": 804, "v01_unit": 9372, "v02_rank_share": 61880,
             "v02_whole_performer": 61880, "audio_long_history": 244772,
-            "v02_history_prefill": 60928}
+            "v02_history_prefill": 60928, "joint_rank_share": 245692}
     for w in W.ALL:
         assert w.n_keys == want[w.name]
     assert W.TINY.cache_len == 552 and W.V02_RANK.cache_len == 60960
     assert W.AUDIO_LONG.cache_len == 244768
     assert W.V02_RANK.latent_elems == 920 * 10 * 128
+
+
+def test_joint_unit_table():
+    """Audio rows first: they see the cache and the unit's 4 audio tokens; the
+    video rows also see the unit's 920 video tokens. The audio rows and keys
+    are the audio workload's own draws (the same streams, first rows)."""
+    w = W.JOINT_RANK
+    assert w.q_unit_begin() == [0, 4, 924] and w.unit_kend() == [244772, 245692]
+    assert w.visible_pairs() == 4 * 244772 + 920 * 245692
+    q, ks, _, _ = G.step_tensors(w, 2, heads=[5])
+    qa, ksa, _, _ = G.step_tensors(W.AUDIO_LONG, 2, heads=[5])
+    assert np.array_equal(q[:, :4], qa) and np.array_equal(ks[:, :4], ksa)
+    ids = G.history_unit_ids(w)
+    assert np.array_equal(ids, G.history_unit_ids(W.AUDIO_LONG))
 
 
 def test_prefill_unit_table():

@@ -27,7 +27,9 @@ class Workload:
     audio_tokens: int       # latent audio tokens per unit
     cached_units: int       # complete prior units in the cache
     query: str              # "video" or "audio": which latent is denoised;
-                            # "prefill": every cached unit's video tokens at once
+                            # "joint": the unit's audio, then video, queries in
+                            # one call; "prefill": every cached unit's video
+                            # tokens at once
     history_audio: bool     # history units also hold their audio tokens
     data_scale: float = 1.0  # Q/K/V ~ N(0,1) * data_scale before bf16 rounding
     steps: int = 4          # denoise steps per unit
@@ -59,9 +61,18 @@ class Workload:
         return self.history_len + (0 if self.prefill else self.slice_tokens)
 
     @property
+    def joint(self) -> bool:
+        """Audio and video queries of the current unit in one call: rows
+        [0, audio) are audio, the rest video; the own tokens are ordered the
+        same way."""
+        return self.query == "joint"
+
+    @property
     def n_q(self) -> int:
         if self.prefill:
             return self.cached_units * self.video_tokens
+        if self.joint:
+            return self.audio_tokens + self.video_tokens
         return self.video_tokens if self.query == "video" else self.audio_tokens
 
     @property
@@ -70,17 +81,24 @@ class Workload:
         return 0 if self.prefill else self.n_q
 
     def q_unit_begin(self) -> list:
-        """First query row of every unit, then n_q (the call's unit table)."""
-        if not self.prefill:
-            return [0, self.n_q]
-        return [u * self.video_tokens for u in range(self.cached_units + 1)]
+        """First query row of every query group, then n_q (the call's unit
+        table)."""
+        if self.prefill:
+            return [u * self.video_tokens for u in range(self.cached_units + 1)]
+        if self.joint:
+            return [0, self.audio_tokens, self.n_q]
+        return [0, self.n_q]
 
     def unit_kend(self) -> list:
-        """Keys visible to each unit of the call: a unit sees the cache up to
-        its own end (streaming: everything, its own tokens included)."""
-        if not self.prefill:
-            return [self.n_keys]
-        return [(u + 1) * self.unit_tokens for u in range(self.cached_units)]
+        """Keys visible to each query group: a unit sees the cache up to its
+        own end (streaming: everything, its own tokens included). Joint: the
+        audio queries see the cache and the unit's audio tokens, the video
+        queries also the unit's video tokens."""
+        if self.prefill:
+            return [(u + 1) * self.unit_tokens for u in range(self.cached_units)]
+        if self.joint:
+            return [self.cache_len + self.audio_tokens, self.n_keys]
+        return [self.n_keys]
 
     @property
     def n_keys(self) -> int:
@@ -169,6 +187,15 @@ V02_PREFILL = Workload(
     video_tokens=920, slice_tokens=32, audio_tokens=0, cached_units=64,
     query="prefill", history_audio=False, steps=1)
 
-ALL = [TINY, V01_UNIT, V02_RANK, V02_WHOLE, AUDIO_LONG, V02_PREFILL]
+JOINT_RANK = Workload(
+    name="joint_rank_share",
+    description="the unit's 4 audio and 920 video queries in one call on one rank's 10 of "
+                "40 heads over the 256-unit history of 920 video + 32 slice + 4 audio tokens "
+                "(245,692 keys): one pass over the cache serves both modalities",
+    heads_total=40, heads=10, head_begin=0, head_dim=128,
+    video_tokens=920, slice_tokens=32, audio_tokens=4, cached_units=256,
+    query="joint", history_audio=True)
+
+ALL = [TINY, V01_UNIT, V02_RANK, V02_WHOLE, AUDIO_LONG, V02_PREFILL, JOINT_RANK]
 STREAMING = [w for w in ALL if not w.prefill]   # the per-unit denoising step
 BY_NAME = {w.name: w for w in ALL}
