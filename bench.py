@@ -57,6 +57,10 @@ def parse():
     p.add_argument("--op-bench", action="store_true",
                    help="instead of the unit step: bandwidth of the cache append (952-token "
                         "40-head slices) and of the Euler update, one JSON line each")
+    p.add_argument("--pipeline", action="store_true",
+                   help="instead of the fixed unit step: --steps consecutive units on a growing "
+                        "cache, each unit's slice appended on a second stream while the previous "
+                        "unit denoises; also timed on one stream")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain copy (the append kernel) of known size, for "
                         "calibrating HBM byte counters")
@@ -246,6 +250,67 @@ def prefill_bench(w, args) -> None:
     print(json.dumps(out), flush=True)
 
 
+def pipeline_units(w, units: int):
+    """Device inputs of `units` consecutive units after the workload's
+    history, and the cache holding that history (room for all units)."""
+    import torch
+
+    from cached_block_causal_amd import KVCache, UnitInputs, kv_append
+    from workloads import gen as G
+    from workloads.device import dev_bits
+    heads = list(range(w.head_begin, w.head_begin + w.heads))
+    cache = KVCache(w.heads, w.head_dim, w.history_len + units * w.unit_tokens)
+    for u in range(w.cached_units):
+        k, v = G.cache_unit_tokens(w, u, heads)
+        kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
+    ins = []
+    for i in range(units):
+        u = w.cached_units + i
+        sk, sv = G.cache_unit_tokens(w, u, range(w.heads_total), w.slice_tokens)
+        steps = [tuple(dev_bits(t) for t in G.step_tensors(w, s, unit=u)) for s in range(w.steps)]
+        x = torch.from_numpy(G.normal_heads(w.seed, G.TAG_X0, u, 0, heads, w.n_q, w.head_dim))
+        ins.append(UnitInputs(dev_bits(G.token_major(sk)), dev_bits(G.token_major(sv)), steps,
+                              x.to("cuda"), steps[-1][1], steps[-1][2], w.head_begin))
+    return cache, ins
+
+
+def pipeline_bench(w, args) -> None:
+    """--steps consecutive units on a growing cache, with the slice appends
+    overlapped on a second stream, and the same units on one stream."""
+    import torch
+
+    from cached_block_causal_amd import run_units
+    cache, ins = pipeline_units(w, args.steps)
+    history_len = cache.len
+    side = torch.cuda.Stream()
+    res = {}
+    for overlap in (True, False, True):
+        for _ in range(max(1, args.warmup)):
+            cache.rewind(history_len)
+            run_units(cache, ins, w.dt, overlap, side, args.splits)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cache.rewind(history_len)
+        t0.record()
+        run_units(cache, ins, w.dt, overlap, side, args.splits)
+        t1.record()
+        torch.cuda.synchronize()
+        res[overlap] = min(res.get(overlap, 1e30), t0.elapsed_time(t1) / args.steps)
+    flops = sum(4 * w.head_dim * w.n_q * (w.cache_len + i * w.unit_tokens + w.n_self) * w.heads
+                for i in range(args.steps)) * w.steps
+    print(json.dumps({
+        "metric": "streaming units on a growing cache, slice appends overlapped on a second "
+                  "stream: attention TFLOP/s and ms per unit",
+        "value": round(flops / (res[True] * args.steps * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res[True], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, as the unit step)",
+        "config": {"workload": w.name, "units": args.steps, "first_cache_len": w.cache_len,
+                   "last_cache_len": w.cache_len + (args.steps - 1) * w.unit_tokens},
+        "one_stream_ms_per_unit": round(res[False], 4),
+        "overlap_saving_ms_per_unit": round(res[False] - res[True], 4)}), flush=True)
+
+
 def calib_copy(steps: int) -> None:
     """Append kernel over a large slice: a plain copy of known size."""
     import torch
@@ -355,6 +420,9 @@ def main():
         return
     if args.op_bench:
         op_bench(args.steps)
+        return
+    if args.pipeline:
+        pipeline_bench(W.BY_NAME[args.workload], args)
         return
 
     w = W.BY_NAME[args.workload]

@@ -6,10 +6,13 @@ script and a thin PyTorch binding; importing the binding needs the built
 library and raises if it is missing.
 """
 __all__ = ["KVCache", "kv_append", "block_causal_attn", "AttnCall", "attn_default_splits",
-           "attn_workspace_bytes", "fm_euler_step"]
+           "attn_workspace_bytes", "fm_euler_step", "UnitInputs", "run_units"]
 
 
 def __getattr__(name):
+    if name in ("UnitInputs", "run_units"):
+        from . import pipeline
+        return getattr(pipeline, name)
     if name in __all__:
         from . import ops
         return getattr(ops, name)
