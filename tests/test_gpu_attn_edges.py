@@ -53,6 +53,38 @@ def test_identical_keys_give_mean_of_values(d):
     assert_close(out, want, "identical keys")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", ["rising", "falling", "spike"])
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_running_max_moves_across_tiles(d, shape, n_splits):
+    """Scores built along one direction: rising by about 10 log2 units per
+    64-key tile (more than the running max may lag, so the output, the
+    denominator and the score offset are rescaled at every tile), falling
+    (the first tile holds the max), or flat with one spike in a middle
+    tile; plus random noise. Every output against the oracle."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(d + len(shape))
+    n, heads, nq = 640, 2, 40
+    j = np.arange(n, dtype=np.float32)
+    if shape == "rising":
+        b = 0.01 * j * np.sqrt(128 / d)
+    elif shape == "falling":
+        b = 0.01 * (n - 1 - j) * np.sqrt(128 / d)
+    else:
+        b = np.where(j == 333, 4.0, 0.0).astype(np.float32)
+    base = np.ones(d, np.float32)
+    k = b[None, :, None] * base[None, None, :] + 0.05 * rng.standard_normal((heads, n, d)).astype(np.float32)
+    ck = G.bf16_rne_bits(k.astype(np.float32))
+    cv = _bits(rng, (heads, n, d))
+    q = G.bf16_rne_bits((np.ones((heads, nq, d), np.float32)
+                         + 0.05 * rng.standard_normal((heads, nq, d)).astype(np.float32)))
+    cache = _cache_with(ck, cv)
+    out = host_bits(block_causal_attn(cache, dev_bits(q), n_splits=n_splits))
+    want = O.attention(q, ck, cv, np.zeros(nq), np.zeros(n), 1 / np.sqrt(d))
+    assert_close(out, want, f"{shape} D {d} splits {n_splits}")
+
+
 RAGGED = [
     # (d, heads, n_q, n_cache, n_self)
     (64, 3, 1, 1, 0),
