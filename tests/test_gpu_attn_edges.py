@@ -140,6 +140,34 @@ def test_units_seeing_part_of_the_cache():
         assert_close(out, want, f"partial visibility splits {n_splits}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_maximum_units_and_splits(d):
+    """The largest unit table (64 units of 1 to 9 keys and 0 to 5 queries,
+    so query and key tiles hold many units) and the largest split count
+    (256, far more splits than key tiles: most splits are empty and must
+    drop out of the merge)."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(64 + d)
+    h = 2
+    unit_keys = rng.integers(1, 10, 64)
+    unit_queries = rng.integers(0, 6, 64)
+    unit_queries[-1] = max(1, unit_queries[-1])
+    nk, nq = int(unit_keys.sum()), int(unit_queries.sum())
+    ck, cv = _bits(rng, (h, nk, d)), _bits(rng, (h, nk, d))
+    q = _bits(rng, (h, nq, d))
+    qb = np.concatenate([[0], np.cumsum(unit_queries)]).tolist()
+    kend = np.cumsum(unit_keys).tolist()
+    cache = _cache_with(ck, cv)
+    ku = np.repeat(np.arange(64), unit_keys)
+    qu = np.repeat(np.arange(64), unit_queries)
+    want = O.attention(q, ck, cv, qu, ku, 1 / np.sqrt(d))
+    for n_splits in (0, 256):
+        out = host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=qb, unit_kend=kend,
+                                          n_splits=n_splits))
+        assert_close(out, want, f"64 units splits {n_splits}")
+
+
 def test_empty_query_set_is_noop():
     need_gpu()
     from cached_block_causal_amd import block_causal_attn
