@@ -469,27 +469,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
 
 // Combine split partials: out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
 // M = max_s lse_s. Bound by HBM (4 * splits * (D + 1) bytes read and 2 * D
-// written per row). D/4 threads per row, 16-byte reads.
-template <int D>
+// written per row). D/4 threads per group, 16-byte reads. With G = 1 a group
+// walks all splits of a row; with G > 1 (many splits, few rows, as in the
+// audio path) G groups take every G-th split of one row and their partial
+// sums (each relative to its own max) are combined through LDS, so a row's
+// loads are spread over G times more threads instead of one serial chain.
+template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_lse,
                                                          uint16_t* __restrict__ out,
                                                          int rows, int n_splits) {
-  constexpr int kTpr = D / 4;
-  constexpr int kRpb = 256 / kTpr;
-  const int row = blockIdx.x * kRpb + threadIdx.x / kTpr;
+  constexpr int kTpr = D / 4;              // threads per group (4 dims each)
+  constexpr int kRpb = 256 / (kTpr * G);   // rows per block
+  const int row_in_block = threadIdx.x / (kTpr * G);
+  const int g = (threadIdx.x / kTpr) % G;
   const int c = threadIdx.x % kTpr;
-  if (row >= rows) return;
+  const int row = blockIdx.x * kRpb + row_in_block;
+  const bool live = row < rows;
   float mx = kNegInf;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[(int64_t)s * rows + row]);
+  if (live)
+    for (int s = g; s < n_splits; s += G) mx = fmaxf(mx, part_lse[(int64_t)s * rows + row]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float lse = part_lse[(int64_t)s * rows + row];
-    const float wgt = lse == kNegInf ? 0.f : fast_exp2(lse - mx);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ((int64_t)s * rows + row) * D + 4 * c);
-    acc += wgt * v;
-    wsum += wgt;
+  if (live)
+    for (int s = g; s < n_splits; s += G) {
+      const float lse = part_lse[(int64_t)s * rows + row];
+      const float wgt = lse == kNegInf ? 0.f : fast_exp2(lse - mx);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ((int64_t)s * rows + row) * D + 4 * c);
+      acc += wgt * v;
+      wsum += wgt;
+    }
+  if constexpr (G > 1) {
+    __shared__ f32x4 s_acc[kRpb][G][kTpr];
+    __shared__ float s_m[kRpb][G], s_w[kRpb][G];
+    s_acc[row_in_block][g][c] = acc;
+    if (c == 0) {
+      s_m[row_in_block][g] = mx;
+      s_w[row_in_block][g] = wsum;
+    }
+    __syncthreads();
+    if (g != 0 || !live) return;
+    float m_all = kNegInf;
+#pragma unroll
+    for (int i = 0; i < G; ++i) m_all = fmaxf(m_all, s_m[row_in_block][i]);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    wsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float mi = s_m[row_in_block][i];
+      const float f = mi == kNegInf ? 0.f : fast_exp2(mi - m_all);
+      acc += f * s_acc[row_in_block][i][c];
+      wsum += f * s_w[row_in_block][i];
+    }
+  } else {
+    if (!live) return;
   }
   const float inv = 1.f / wsum;
   *reinterpret_cast<u32x2*>(out + (int64_t)row * D + 4 * c) =
@@ -511,14 +544,25 @@ hipError_t launch_attn_merge(const float* part_o, const float* part_lse, uint16_
                              int heads, int n_q, int head_dim, int n_splits,
                              hipStream_t stream) {
   const int rows = heads * n_q;
-  const int rpb = 256 / (head_dim / 4);
+  // many splits: spread each row over 8 groups of threads
+  const int groups = n_splits >= 16 ? 8 : 1;
+  const int rpb = 256 / (head_dim / 4 * groups);
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(grid), dim3(256), 0, stream,
-                       part_o, part_lse, out, rows, n_splits);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(grid), dim3(256), 0, stream,
-                       part_o, part_lse, out, rows, n_splits);
+  if (head_dim == 128) {
+    if (groups > 1)
+      hipLaunchKernelGGL((attn_merge_kernel<128, 8>), dim3(grid), dim3(256), 0, stream,
+                         part_o, part_lse, out, rows, n_splits);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<128, 1>), dim3(grid), dim3(256), 0, stream,
+                         part_o, part_lse, out, rows, n_splits);
+  } else {
+    if (groups > 1)
+      hipLaunchKernelGGL((attn_merge_kernel<64, 8>), dim3(grid), dim3(256), 0, stream,
+                         part_o, part_lse, out, rows, n_splits);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<64, 1>), dim3(grid), dim3(256), 0, stream,
+                         part_o, part_lse, out, rows, n_splits);
+  }
   return hipGetLastError();
 }
 
