@@ -143,7 +143,9 @@ def roofline(w, attn_avg_ms: float, attn_min_ms: float) -> dict:
     gbs = kv / (attn_avg_ms * 1e-3) / 1e9
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     hbm = flops / kv < ridge
-    r = {"kernel": "attn_partial_kernel<%d>" % w.head_dim, "bound": "hbm" if hbm else "mfma",
+    # the library runs its narrow kernel for calls with at most 32 queries
+    kernel = "attn_narrow_kernel" if w.n_q <= 32 else "attn_partial_kernel"
+    r = {"kernel": "%s<%d>" % (kernel, w.head_dim), "bound": "hbm" if hbm else "mfma",
          "achieved": round(gbs if hbm else tf, 2), "peak": PEAK_HBM_GBS if hbm else PEAK_BF16_TFLOPS,
          "unit": "GB/s" if hbm else "TFLOP/s",
          "frac": round((gbs / PEAK_HBM_GBS) if hbm else (tf / PEAK_BF16_TFLOPS), 4),

@@ -47,6 +47,11 @@
 //    mask is applied only to tiles that reach past its first row's keys.
 //  * Rows past the visible range read as zeros and are masked to -inf, so
 //    unused cache capacity never reaches the arithmetic.
+//  * Calls with at most 32 queries (the handful of audio tokens of a unit)
+//    run a narrow kernel instead: one wave per (head, split) over 32-key
+//    tiles, with its own two LDS stages and no barrier. Such a call is bound
+//    by the K/V stream; the narrow form spends 4x fewer MFMAs on empty query
+//    rows and fills the chip with more, shorter streams.
 #include <math.h>
 
 #include "ws_device.hpp"
@@ -88,6 +93,13 @@ template <int G>
 __device__ __forceinline__ void dma_group(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, G * 64, 0, 0);
 }
+
+// s_waitcnt operand that waits for vector memory counter <= n (0..63) only:
+// vmcnt is split over bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8)
+// are left at their maxima.
+constexpr int vmcnt_only(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// s_waitcnt operand that waits for lgkmcnt == 0 only
+constexpr int kLgkmZero = 0xC07F;
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int byte_off) {
   return *reinterpret_cast<const u32x4*>(base + byte_off);
@@ -467,6 +479,227 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   }
 }
 
+// Narrow calls (all queries in one 32-row block, e.g. the 4 audio queries of
+// a unit): the main kernel would keep three of its four waves idle, and the
+// call is bound by HBM. Here one workgroup is one wave and one (head, split):
+// it streams 32-key tiles of K and V through its own two LDS stages (16 KB
+// each at D = 128) with no barrier, and computes
+// S^T (8 MFMAs), the softmax of 16 scores per lane and O^T += V^T P^T (8
+// MFMAs) per tile. Partials go through the same workspace and merge as the
+// main kernel's.
+template <int D>
+__global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
+  using T = Tile<D>;
+  constexpr int kN = kAttnNarrowN;            // keys per tile
+  constexpr int kGB = kN * 64;                // one 64-byte column group of a tile
+  constexpr int kSB = T::kGroups * kGB;       // one stage
+  constexpr int kLoads = (kN / 16) * T::kGroups;  // 1 KB loads per tile and operand
+  __shared__ __attribute__((aligned(16))) char k_st0[kSB];
+  __shared__ __attribute__((aligned(16))) char k_st1[kSB];
+  __shared__ __attribute__((aligned(16))) char v_st0[kSB];
+  __shared__ __attribute__((aligned(16))) char v_st1[kSB];
+
+  const int w = blockIdx.x;
+  if (w >= a.n_items) return;
+  const int split = w % a.n_splits;
+  const int h = w / a.n_splits;
+  const int lane = threadIdx.x;
+  const int lrow = lane & 31;
+  const int half = lane >> 5;
+
+  const int kmin = row_kend(a, 0);
+  const int kmax = row_kend(a, a.n_q - 1);
+  const int cache_rows = min(a.len, kmax);
+  const int self_rows = max(0, kmax - a.len);
+  const int n_ct = (cache_rows + kN - 1) / kN;
+  const int n_kt = n_ct + (self_rows + kN - 1) / kN;
+  const int t_begin = (int)((int64_t)split * n_kt / a.n_splits);
+  const int n_t = (int)((int64_t)(split + 1) * n_kt / a.n_splits) - t_begin;
+
+  const uint16_t* kc_h = a.kc + h * a.cache_head_stride;
+  const uint16_t* vc_h = a.vc + h * a.cache_head_stride;
+  const uint16_t* ks_h = a.ks + (int64_t)h * a.n_self * D;
+  const uint16_t* vs_h = a.vs + (int64_t)h * a.n_self * D;
+
+  const int qrow = lrow;
+  int kend = 0;
+  for (int u = 0; u < a.n_units; ++u) kend = qrow >= a.q_unit_begin[u] ? a.unit_kend[u] : kend;
+  if (qrow >= a.n_q) kend = 0;
+  u32x4 qf[T::kDSteps];
+  {
+    const uint16_t* qp = a.q + ((int64_t)h * a.n_q + qrow) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+      qf[ks] = qrow < a.n_q ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qf[ks][e] = pack_bf16x2(bf16_lo(qf[ks][e]) * a.scale_log2, bf16_hi(qf[ks][e]) * a.scale_log2);
+  }
+  f32x16 o[T::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < T::kDBlocks; ++db) o[db] = f32x16{};
+  float m_run = kNegInf, m_off = 0.f, l_run = 0.f;
+  f32x16 neg_off = f32x16{};
+
+  // LDS layout as in the main kernel: byte (G, row, slot) = G*kGB + row*64 +
+  // slot*16 holds chunk 4G + (slot ^ ((row >> 2) & 3)); lane l of load b
+  // writes row 16b + l/4, slot l%4.
+  const uint32_t dma_off = (uint32_t)((lane >> 2) * D * 2 + (((lane & 3) ^ (lane >> 4)) * 16));
+  const int k_ofs[2] = {lrow * 64 + (((0 + half) ^ ((lrow >> 2) & 3)) * 16),
+                        lrow * 64 + (((2 + half) ^ ((lrow >> 2) & 3)) * 16)};
+  const int v_s = (lane >> 2) & 3, v_q = lane & 3, v_g1 = (lane >> 4) & 1;
+  const int v_u = 2 * v_g1 + (v_q >> 1);
+  const int v_ofs[2] = {(4 * half + v_s) * 64 + ((v_u ^ (0 + half)) * 16) + 8 * (v_q & 1),
+                        (4 * half + v_s) * 64 + ((v_u ^ (2 + half)) * 16) + 8 * (v_q & 1)};
+
+  struct TileLoc {
+    int abs_base, rows;
+    const uint16_t *k, *v;
+  };
+  // Each wave starts its sweep at a rotated tile of its range (any order
+  // gives the same softmax): waves that run in step would otherwise read
+  // addresses a fixed stride apart and pile onto the same memory channels.
+  const int rot = n_t > 0 ? (int)(((uint32_t)w * 2654435761u) % (uint32_t)n_t) : 0;
+  auto locate = [&](int r) {  // r in [0, n_t + 2); r >= n_t is an empty tile
+    const int rr = r + rot < n_t ? r + rot : r + rot - n_t;
+    const int t = t_begin + rr;
+    const bool own = t >= n_ct;
+    const int local = (own ? t - n_ct : t) * kN;
+    TileLoc L;
+    L.abs_base = own ? a.len + local : local;
+    L.rows = __builtin_amdgcn_readfirstlane(
+        r < n_t ? max(0, min(kN, (own ? self_rows : cache_rows) - local)) : 0);
+    L.k = (own ? ks_h : kc_h) + (int64_t)local * D;
+    L.v = (own ? vs_h : vc_h) + (int64_t)local * D;
+    return L;
+  };
+  auto dma_tile = [&](const uint16_t* rows_ptr, int rows, char* stage) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows_ptr, (uint32_t)rows * D * 2);
+#pragma unroll
+    for (int b = 0; b < kN / 16; ++b) {
+      char* dst = stage + b * 1024;
+      const uint32_t off = dma_off + b * 16 * D * 2;
+      dma_group<0>(rs, dst, off);
+      dma_group<1>(rs, dst + kGB, off);
+      if constexpr (T::kGroups == 4) {
+        dma_group<2>(rs, dst + 2 * kGB, off);
+        dma_group<3>(rs, dst + 3 * kGB, off);
+      }
+    }
+  };
+  auto dma = [&](int r, char* ks_stage, char* vs_stage) {
+    const TileLoc L = locate(r);
+    dma_tile(L.k, L.rows, ks_stage);
+    dma_tile(L.v, L.rows, vs_stage);
+  };
+
+  auto tile = [&](int r, const char* kst, const char* vst) {
+    // S^T of the tile's 32 keys (lane: query lrow, 16 keys)
+    f32x16 sc = neg_off;
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+      sc = mfma32x32x16(lds_read16(kst, (ks >> 1) * kGB + k_ofs[ks & 1]), qf[ks], sc);
+    // mask the keys past the tile's rows or this row's visible range
+    const TileLoc L = locate(r);
+    if (__builtin_expect(L.rows < kN || L.abs_base + kN > kmin, 0)) {
+      const int lim = min(L.rows, kend - L.abs_base);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = 8 * (rr >> 2) + 4 * half + (rr & 3);
+        sc[rr] = key < lim ? sc[rr] : kNegInf;
+      }
+    }
+    float mloc = kNegInf;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) mloc = fmaxf(mloc, sc[rr]);
+    const float mt = half_swap_max(mloc) + m_off;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0, 0)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < T::kDBlocks; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      const float off_new = m_new == kNegInf ? 0.f : m_new;
+      sc += m_off - off_new;
+      m_off = off_new;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) neg_off[rr] = -off_new;
+    }
+    // P in bf16 (B operand of O^T += V^T P^T) and the denominator
+    u32x4 pb[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w2 = pack_bf16x2(fast_exp2(sc[2 * j]), fast_exp2(sc[2 * j + 1]));
+      pb[j >> 2][j & 3] = w2;
+      l_run = add_bf16x2(w2, l_run);
+    }
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const char* b = vst + db * kGB + 16 * ks2 * 64;
+        const u32x2 lo = lds_read_tr(b, v_ofs[0]);
+        const u32x2 hi = lds_read_tr(b + 8 * 64, v_ofs[1]);
+        o[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks2], o[db]);
+      }
+  };
+
+  // Tile r reads stage r % 2 while the loads of tile r+1 fill the other one.
+  // Only this wave touches its stages: before loads overwrite a stage, its
+  // LDS reads (of tile r-1) must have returned (lgkmcnt 0); before a tile is
+  // read, its own loads must have landed (vmcnt <= the next tile's loads).
+  if (n_t > 0) dma(0, k_st0, v_st0);
+  for (int r = 0; r < n_t; r += 2) {
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+    __asm__ volatile("" ::: "memory");
+    dma(r + 1, k_st1, v_st1);  // past the split's end: empty ranges, nothing read
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLoads));
+    __asm__ volatile("" ::: "memory");
+    tile(r, k_st0, v_st0);
+    if (r + 1 >= n_t) break;
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+    __asm__ volatile("" ::: "memory");
+    dma(r + 2, k_st0, v_st0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLoads));
+    __asm__ volatile("" ::: "memory");
+    tile(r + 1, k_st1, v_st1);
+  }
+  // loads past the split's end may still be in flight: they must land before
+  // the workgroup exits and its LDS is handed to another
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const float l_tot = half_swap_sum(l_run);
+  if (qrow >= a.n_q) return;
+  const int64_t row_id = (int64_t)h * a.n_q + qrow;
+  if (a.n_splits == 1) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = a.out + row_id * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<u32x2*>(op + db * 32 + 8 * g) =
+            u32x2{pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                  pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+  } else {
+    const int64_t prow = (int64_t)split * a.heads * a.n_q + row_id;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = a.part_o + prow * D + 4 * half;
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g) =
+            f32x4{o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv,
+                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+    if (half == 0) a.part_lse[prow] = l_tot > 0.f ? m_run + log2f(l_tot) : kNegInf;
+  }
+}
+
 // Combine split partials: out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
 // M = max_s lse_s. Bound by HBM (4 * splits * (D + 1) bytes read and 2 * D
 // written per row). D/4 threads per group, 16-byte reads. With G = 1 a group
@@ -532,6 +765,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 }  // namespace
 
 hipError_t launch_attn_partial(const AttnArgs& a, int head_dim, hipStream_t stream) {
+  if (attn_narrow(a.n_q)) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(attn_narrow_kernel<128>, dim3(a.n_items), dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(attn_narrow_kernel<64>, dim3(a.n_items), dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)((a.n_items + 7) / 8 * 8);
   if (head_dim == 128)
     hipLaunchKernelGGL(attn_partial_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);

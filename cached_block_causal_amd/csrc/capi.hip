@@ -52,16 +52,31 @@ ws_status check_cache(const ws_kv_cache* c) {
 // ceil(items * s / slots) rounds, plus the partials' round trip through
 // memory at ~4 TB/s when s > 1.
 constexpr int kSlots = 256 * 2;  // 256 CUs x 2 resident workgroups
+// Resident one-wave workgroups of the narrow kernel (32 KB of LDS each):
+// measured, four per CU stay resident; the run time steps up once a grid
+// exceeds 1024 of them.
+constexpr int kNarrowSlots = 256 * 4;
 constexpr int kMaxSplits = 256;
 
 int32_t default_splits(int32_t heads, int32_t n_q, int32_t head_dim, int64_t n_keys) {
   if (heads <= 0 || n_q <= 0 || n_keys <= 0 || head_dim <= 0) return 1;
   const int64_t items = (int64_t)heads * ((n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM);
-  const int64_t tiles = (n_keys + ws::kAttnBlockN - 1) / ws::kAttnBlockN;
-  const double t_tile_us = 1.7 * head_dim / 128.0;
+  const bool narrow = ws::attn_narrow(n_q);
+  const int64_t tiles = (n_keys + (narrow ? ws::kAttnNarrowN : ws::kAttnBlockN) - 1) /
+                        (narrow ? ws::kAttnNarrowN : ws::kAttnBlockN);
   int64_t max_s = tiles / 4;
   if (max_s > kMaxSplits) max_s = kMaxSplits;
   if (max_s < 1) max_s = 1;
+  if (narrow) {
+    // The narrow kernel streams K/V at the memory's pace, one wave per item:
+    // fill one round of resident waves and no more. A second round leaves
+    // its few waves streaming alone at the end (40 heads over 244,772 keys:
+    // 1,000 waves take 0.83 ms, 1,040 waves 1.01 ms).
+    int64_t s = kNarrowSlots / items;
+    if (s > max_s) s = max_s;
+    return (int32_t)(s < 1 ? 1 : s);
+  }
+  const double t_tile_us = 1.7 * head_dim / 128.0;
   int32_t best = 1;
   double best_cost = 1e300;
   for (int64_t s = 1; s <= max_s; ++s) {

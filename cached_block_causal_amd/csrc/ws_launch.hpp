@@ -40,6 +40,10 @@ struct AttnArgs {
 constexpr int kAttnBlockM = 128;
 // Keys per LDS tile.
 constexpr int kAttnBlockN = 64;
+// Calls whose queries all fit one 32-row block run the narrow kernel: one
+// wave per (head, split) over 32-key tiles.
+constexpr int kAttnNarrowN = 32;
+inline bool attn_narrow(int n_q) { return n_q <= 32; }
 
 hipError_t launch_attn_partial(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_merge(const float* part_o, const float* part_lse, uint16_t* out,

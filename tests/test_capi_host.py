@@ -131,3 +131,9 @@ def test_split_planning_is_host_only_and_sized(lib):
         assert 1 <= s <= 256
         need = lib.ws_attn_workspace_bytes(heads, nq, d, s)
         assert (s == 1 and need == 0) or need >= s * heads * nq * (d + 1) * 4
+    # at most 32 queries: one round of 1024 one-wave workgroups, at most a
+    # quarter of the 32-key tiles per split
+    assert lib.ws_attn_default_splits(40, 4, 128, 244772) == 25
+    assert lib.ws_attn_default_splits(10, 32, 128, 244772) == 102
+    assert lib.ws_attn_default_splits(3, 1, 64, 200) == 1
+    assert lib.ws_attn_default_splits(2000, 4, 128, 244772) == 1

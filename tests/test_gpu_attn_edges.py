@@ -56,16 +56,18 @@ def test_identical_keys_give_mean_of_values(d):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("shape", ["rising", "falling", "spike"])
 @pytest.mark.parametrize("n_splits", [1, 3])
-def test_running_max_moves_across_tiles(d, shape, n_splits):
+@pytest.mark.parametrize("nq", [40, 4])
+def test_running_max_moves_across_tiles(d, shape, n_splits, nq):
     """Scores built along one direction: rising by about 10 log2 units per
     64-key tile (more than the running max may lag, so the output, the
-    denominator and the score offset are rescaled at every tile), falling
-    (the first tile holds the max), or flat with one spike in a middle
-    tile; plus random noise. Every output against the oracle."""
+    denominator and the score offset are rescaled at every tile or every
+    other 32-key tile), falling (the first tile holds the max), or flat with
+    one spike in a middle tile; plus random noise. 40 queries run the main
+    kernel, 4 the narrow one. Every output against the oracle."""
     need_gpu()
     from cached_block_causal_amd import block_causal_attn
     rng = np.random.default_rng(d + len(shape))
-    n, heads, nq = 640, 2, 40
+    n, heads = 640, 2
     j = np.arange(n, dtype=np.float32)
     if shape == "rising":
         b = 0.01 * j * np.sqrt(128 / d)
@@ -82,7 +84,7 @@ def test_running_max_moves_across_tiles(d, shape, n_splits):
     cache = _cache_with(ck, cv)
     out = host_bits(block_causal_attn(cache, dev_bits(q), n_splits=n_splits))
     want = O.attention(q, ck, cv, np.zeros(nq), np.zeros(n), 1 / np.sqrt(d))
-    assert_close(out, want, f"{shape} D {d} splits {n_splits}")
+    assert_close(out, want, f"{shape} D {d} splits {n_splits} queries {nq}")
 
 
 RAGGED = [
@@ -138,6 +140,32 @@ def test_units_seeing_part_of_the_cache():
         q_unit = np.concatenate([np.full(qb[u + 1] - qb[u], u) for u in range(len(kend))])
         want = O.attention(q, k, v, q_unit, key_unit, 1 / np.sqrt(d))
         assert_close(out, want, f"partial visibility splits {n_splits}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_narrow_call_with_units(d):
+    """At most 32 queries (the narrow kernel): four units, one of them empty,
+    whose visible ranges end inside the cache, mid-tile and inside the own
+    tokens; default, one, five and 256 splits."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn
+    rng = np.random.default_rng(32 + d)
+    h, nc, ns = 3, 333, 41
+    ck, cv = _bits(rng, (h, nc, d)), _bits(rng, (h, nc, d))
+    sk, sv = _bits(rng, (h, ns, d)), _bits(rng, (h, ns, d))
+    qb = [0, 4, 4, 17, 32]
+    kend = [100, 250, 333 + 7, 374]
+    q = _bits(rng, (h, qb[-1], d))
+    cache = _cache_with(ck, cv)
+    k = np.concatenate([ck, sk], axis=1)
+    v = np.concatenate([cv, sv], axis=1)
+    key_unit = np.searchsorted(np.array(kend), np.arange(nc + ns), side="right")
+    q_unit = np.concatenate([np.full(qb[u + 1] - qb[u], u) for u in range(len(kend))])
+    want = O.attention(q, k, v, q_unit, key_unit, 1 / np.sqrt(d))
+    for n_splits in (0, 1, 5, 256):
+        out = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(sk), dev_bits(sv),
+                                          q_unit_begin=qb, unit_kend=kend, n_splits=n_splits))
+        assert_close(out, want, f"narrow units D {d} splits {n_splits}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
