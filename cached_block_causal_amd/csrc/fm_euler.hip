@@ -6,7 +6,9 @@
 // x is the float32 latent share, v the bf16 velocity. Each element is one
 // fused multiply-add, so the result is x + dt*v rounded once to nearest-even.
 // Bound by HBM: 4 + 4 + 2 = 10 bytes per element. Each thread handles two
-// groups of 8 elements per iteration (16-byte accesses, loads issued first).
+// groups of 8 elements per iteration (16-byte accesses, loads issued first),
+// all non-temporal: between two steps the attention streams far more than the
+// caches hold, so nothing of x or v would still be cached.
 #include "ws_device.hpp"
 #include "ws_launch.hpp"
 
@@ -39,9 +41,9 @@ __global__ __launch_bounds__(256) void fm_euler_kernel(float* __restrict__ x,
       const int64_t i = i0 + (int64_t)j * blockDim.x;
       if (i < n8) {
         const f32x4* xp = reinterpret_cast<const f32x4*>(x + i * 8);
-        a[j] = xp[0];
-        b[j] = xp[1];
-        w[j] = *reinterpret_cast<const u32x4*>(v + i * 8);
+        a[j] = __builtin_nontemporal_load(xp);
+        b[j] = __builtin_nontemporal_load(xp + 1);
+        w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + i * 8));
       }
     }
 #pragma unroll
@@ -50,8 +52,8 @@ __global__ __launch_bounds__(256) void fm_euler_kernel(float* __restrict__ x,
       if (i < n8) {
         euler8(a[j], b[j], w[j], dt);
         f32x4* xp = reinterpret_cast<f32x4*>(x + i * 8);
-        xp[0] = a[j];
-        xp[1] = b[j];
+        __builtin_nontemporal_store(a[j], xp);
+        __builtin_nontemporal_store(b[j], xp + 1);
       }
     }
   }

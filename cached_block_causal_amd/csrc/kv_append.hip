@@ -9,7 +9,10 @@
 // 16-byte chunks of one head (the D/8 chunks of a row fastest, then tokens):
 // each thread issues its four loads before its four stores, consecutive lanes
 // write consecutive cache addresses and read whole 128/256-byte rows of the
-// source, and the (token, chunk) split is a shift and a mask.
+// source, and the (token, chunk) split is a shift and a mask. Loads and stores
+// are non-temporal: neither side is re-read before it would have left the
+// caches, and streaming them past the caches made a 952-token, 40-head append
+// about 20 % faster.
 #include "ws_device.hpp"
 #include "ws_launch.hpp"
 
@@ -38,14 +41,15 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   for (int j = 0; j < kAppendUnroll; ++j) {  // all loads first, then the stores
     const int i = base + j * 256;
     if (i < per_head)
-      v[j] = *reinterpret_cast<const u32x4*>(src + src_h + (int64_t)(i >> log2_cpr) * src_t +
-                                             (i & cmask) * 8);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          src + src_h + (int64_t)(i >> log2_cpr) * src_t + (i & cmask) * 8));
   }
 #pragma unroll
   for (int j = 0; j < kAppendUnroll; ++j) {
     const int i = base + j * 256;
     if (i < per_head)
-      *reinterpret_cast<u32x4*>(dst_h + (int64_t)(i >> log2_cpr) * head_dim + (i & cmask) * 8) = v[j];
+      __builtin_nontemporal_store(
+          v[j], reinterpret_cast<u32x4*>(dst_h + (int64_t)(i >> log2_cpr) * head_dim + (i & cmask) * 8));
   }
 }
 
