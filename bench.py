@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -134,10 +135,17 @@ def cpu_baseline(w, budget_s: float):
                       f"each), {elapsed:.2f} s of compute; host has {os.cpu_count()} logical CPUs"}
 
 
-def roofline(w, attn_avg_ms: float, attn_min_ms: float) -> dict:
+def roofline(w, attn_ms: list) -> dict:
     """The attention kernel against the roofline that bounds it: the bf16
     MFMA peak above the ridge point (peak FLOP/s / peak B/s), HBM below it.
-    Both fractions are given."""
+    Both fractions are given, from the average of the timed launches; their
+    minimum and 10th/50th/90th percentiles (nearest rank) are reported too."""
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    srt = sorted(attn_ms)
+
+    def pct(p):
+        return srt[max(1, math.ceil(p / 100 * len(srt))) - 1]
+
     flops, kv = w.attn_flops(), w.attn_kv_bytes()
     tf = flops / (attn_avg_ms * 1e-3) / 1e12
     gbs = kv / (attn_avg_ms * 1e-3) / 1e9
@@ -152,7 +160,9 @@ def roofline(w, attn_avg_ms: float, attn_min_ms: float) -> dict:
          "traffic": stored_traffic(w.name),
          "mfma_tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
          "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-         "launch_ms_avg": round(attn_avg_ms, 5), "launch_ms_min": round(attn_min_ms, 5)}
+         "launch_ms_avg": round(attn_avg_ms, 5), "launch_ms_min": round(srt[0], 5),
+         "launch_ms_p10": round(pct(10), 5), "launch_ms_p50": round(pct(50), 5),
+         "launch_ms_p90": round(pct(90), 5), "launches_timed": len(attn_ms)}
     return r
 
 
@@ -243,7 +253,7 @@ def prefill_bench(w, args) -> None:
                    "head_dim": w.head_dim, "n_q": w.n_q, "n_keys": w.n_keys,
                    "units": w.cached_units, "visible_pairs_per_head": w.visible_pairs(),
                    "splits": call.splits},
-        "roofline": roofline(w, sum(attn_ms) / len(attn_ms), min(attn_ms)),
+        "roofline": roofline(w, attn_ms),
         "host_wall_s": round(wall, 3),
         "setup_s": round(setup_s, 2),
     }
@@ -523,7 +533,7 @@ def main():
                    "head_dim": w.head_dim, "n_q": w.n_q, "cache_len": w.cache_len,
                    "n_keys": w.n_keys, "denoise_steps": w.steps, "splits": splits,
                    "slice_tokens": w.slice_tokens, "commit_tokens": w.n_self},
-        "roofline": roofline(w, attn_avg_ms, min(attn_ms)),
+        "roofline": roofline(w, attn_ms),
         "us_per_unit": round(ms_per_step * 1e3, 1),
         "unit_budget_frac": round(ms_per_step / UNIT_BUDGET_MS, 5),
         "attention_layers_per_unit_budget": int(UNIT_BUDGET_MS // ms_per_step),
