@@ -483,10 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
 // a unit): the main kernel would keep three of its four waves idle, and the
 // call is bound by HBM. Here one workgroup is one wave and one (head, split):
 // it streams 32-key tiles of K and V through its own two LDS stages (16 KB
-// each at D = 128) with no barrier, and computes
-// S^T (8 MFMAs), the softmax of 16 scores per lane and O^T += V^T P^T (8
-// MFMAs) per tile. Partials go through the same workspace and merge as the
-// main kernel's.
+// each at D = 128) with no barrier, and per tile computes S^T (8 MFMAs at
+// D = 128), the softmax of 16 scores per lane and O^T += V^T P^T (8 MFMAs).
+// Partials go through the same workspace and merge as the main kernel's.
 template <int D>
 __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   using T = Tile<D>;
@@ -559,13 +558,8 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
     int abs_base, rows;
     const uint16_t *k, *v;
   };
-  // Each wave starts its sweep at a rotated tile of its range (any order
-  // gives the same softmax): waves that run in step would otherwise read
-  // addresses a fixed stride apart and pile onto the same memory channels.
-  const int rot = n_t > 0 ? (int)(((uint32_t)w * 2654435761u) % (uint32_t)n_t) : 0;
   auto locate = [&](int r) {  // r in [0, n_t + 2); r >= n_t is an empty tile
-    const int rr = r + rot < n_t ? r + rot : r + rot - n_t;
-    const int t = t_begin + rr;
+    const int t = t_begin + r;
     const bool own = t >= n_ct;
     const int local = (own ? t - n_ct : t) * kN;
     TileLoc L;
