@@ -220,3 +220,47 @@ def test_errors_are_reported_before_launch():
     with pytest.raises(WsError) as e:
         AttnCall(cache, q, n_splits=4, workspace=small).run()
     assert e.value.status == WS_ERR_WORKSPACE
+
+
+LONG = [
+    # (d, heads, n_q, n_cache, n_self, units): long caches outside the seven
+    # workloads; the narrow kernel at D = 64 and with a unit table, and the
+    # 128-row kernel at D = 64, at the library's default split counts
+    (64, 16, 4, 60000, 4, 1),
+    (64, 8, 32, 40000, 0, 8),
+    (64, 6, 252, 20000, 252, 1),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[str(c) for c in LONG])
+def test_long_caches_sampled_heads(case):
+    """Every output of two heads (the first and the last) against the oracle."""
+    need_gpu()
+    from cached_block_causal_amd import attn_default_splits, block_causal_attn
+    d, h, nq, nc, ns, units = case
+    rng = np.random.default_rng(nc + nq)
+    ck, cv = _bits(rng, (h, nc, d)), _bits(rng, (h, nc, d))
+    q = _bits(rng, (h, nq, d))
+    sk = _bits(rng, (h, ns, d)) if ns else None
+    sv = _bits(rng, (h, ns, d)) if ns else None
+    cache = _cache_with(ck, cv)
+    nk = nc + ns
+    if units == 1:
+        qb, kend = [0, nq], [nk]
+        q_unit, key_unit = np.zeros(nq), np.zeros(nk)
+    else:
+        # unit u: queries [4u, 4u + 4), keys up to an end spread over the cache
+        qb = list(range(0, nq + 1, nq // units))
+        kend = [int(nk * (u + 1) / units) - (7 if u + 1 < units else 0) for u in range(units)]
+        key_unit = np.searchsorted(np.array(kend), np.arange(nk), side="right")
+        q_unit = np.repeat(np.arange(units), nq // units)
+    assert attn_default_splits(h, nq, d, nk) > 1
+    out = host_bits(block_causal_attn(cache, dev_bits(q), dev_bits(sk) if ns else None,
+                                      dev_bits(sv) if ns else None, q_unit_begin=qb,
+                                      unit_kend=kend))
+    k = np.concatenate([ck, sk], axis=1) if ns else ck
+    v = np.concatenate([cv, sv], axis=1) if ns else cv
+    for hh in (0, h - 1):
+        want = O.attention(q[hh:hh + 1], k[hh:hh + 1], v[hh:hh + 1], q_unit, key_unit,
+                           1 / np.sqrt(d))
+        assert_close(out[hh:hh + 1], want, f"{case} head {hh}")
