@@ -18,9 +18,11 @@ from tests.gpu_common import (assert_close, dev_bits, fill_history, host_bits, n
 pytestmark = pytest.mark.gpu
 
 
-def _streaming_case(w, steps, heads_sampled=None):
+def _streaming_case(w, steps, heads_sampled=None, rows_sampled=None):
     """Run the streaming step of workload w on the GPU for the given denoise
-    steps; compare all heads (heads_sampled None) or the sampled heads."""
+    steps; compare all heads (heads_sampled None) or the sampled heads, on
+    every query row (rows_sampled None) or the sampled rows (rows are
+    independent, so the oracle computes just those)."""
     from cached_block_causal_amd import AttnCall
     print(f"attn {w.name} steps {steps} heads {heads_sampled}", flush=True)
     cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
@@ -42,8 +44,11 @@ def _streaming_case(w, steps, heads_sampled=None):
         call.merge()
         assert np.array_equal(host_bits(call.out), out)
         k, v, ku = O.streaming_keys(hk, hv, w.cache_len, ids, ks[sel], vs[sel], w.current_unit)
-        want = O.attention(q[sel], k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(w.head_dim))
-        results.append(assert_close(out[sel], want, f"{w.name} step {s}"))
+        rows = slice(None) if rows_sampled is None else list(rows_sampled)
+        qs = q[sel][:, rows]
+        want = O.attention(qs, k, v, np.full(qs.shape[1], w.current_unit), ku,
+                           1 / np.sqrt(w.head_dim))
+        results.append(assert_close(out[sel][:, rows], want, f"{w.name} step {s}"))
     print(results, flush=True)
 
 
@@ -67,6 +72,29 @@ def test_v02_rank_share_sampled_heads():
 def test_v02_whole_performer_sampled_heads():
     need_gpu()
     _streaming_case(W.V02_WHOLE, [0], heads_sampled=[0, 21, 39])
+
+
+def _sampled_rows(n_q, n, seed):
+    """Seeded rows plus the edges of every 128-row query tile."""
+    rng = np.random.default_rng(seed)
+    edges = {0, n_q - 1} | {t for t in range(128, n_q, 128)} | {t - 1 for t in range(128, n_q, 128)}
+    return sorted(edges | set(rng.choice(n_q, n, replace=False).tolist()))
+
+
+@pytest.mark.timeout(300)
+def test_v02_rank_share_later_steps_sampled_rows():
+    """Denoise steps 1-3 (fresh queries and own tokens per step) on sampled
+    rows of two heads."""
+    need_gpu()
+    _streaming_case(W.V02_RANK, [1, 2, 3], heads_sampled=[3, 6],
+                    rows_sampled=_sampled_rows(W.V02_RANK.n_q, 64, 1))
+
+
+@pytest.mark.timeout(300)
+def test_v02_whole_performer_later_steps_sampled_rows():
+    need_gpu()
+    _streaming_case(W.V02_WHOLE, [1, 2, 3], heads_sampled=[7, 30],
+                    rows_sampled=_sampled_rows(W.V02_WHOLE.n_q, 64, 2))
 
 
 @pytest.mark.timeout(600)
