@@ -89,6 +89,20 @@ def stored_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def blas_info():
+    """(threads, "vendor version") of the BLAS NumPy uses, for the CPU baseline."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover - informational only
+        libs = []
+    if not libs:
+        return os.cpu_count() or 1, "unknown"
+    lib = max(libs, key=lambda i: i.get("num_threads", 1))
+    return (int(lib.get("num_threads", 1)),
+            f"{lib.get('internal_api', '?')} {lib.get('version', '')}".strip())
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the fp64 oracle on a bounded sample of the same workload: whole
     (denoise step, head) attention problems (all query rows over all keys),
@@ -97,12 +111,7 @@ def cpu_baseline(w, budget_s: float):
 
     import oracle as O
     from workloads import gen as G
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - informational only
-        threads = os.cpu_count() or 1
+    threads, blas = blas_info()
     ids = G.history_unit_ids(w)
     done, flops, elapsed = 0, 0, 0.0
     hist = {}
@@ -128,11 +137,24 @@ def cpu_baseline(w, budget_s: float):
         if elapsed >= budget_s:
             break
         hist = hist if len(hist) * w.cache_len * w.head_dim * 4 < (2 << 30) else {}
+    # the other two steps of the unit, once each: the slice append into a
+    # cache of this length and one Euler step of the unit's latent
+    ck = np.zeros((w.heads, w.cache_len + w.slice_tokens, w.head_dim), np.uint16)
+    sk = np.zeros((w.slice_tokens, w.heads_total, w.head_dim), np.uint16)
+    t0 = time.perf_counter()
+    O.kv_append(ck, ck, w.cache_len, sk, sk, w.head_begin)
+    append_ms = (time.perf_counter() - t0) * 1e3
+    n_el = w.n_q * w.heads * w.head_dim
+    t0 = time.perf_counter()
+    O.fm_euler_state(np.zeros(n_el, np.float32), np.zeros(n_el, np.uint16), w.dt)
+    euler_ms = (time.perf_counter() - t0) * 1e3
     return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 NumPy oracle on {done} of {w.steps * w.heads} (denoise step, head) "
                       f"attention problems of this workload ({w.n_q} queries x {w.n_keys} keys "
-                      f"each), {elapsed:.2f} s of compute; host has {os.cpu_count()} logical CPUs"}
+                      f"each), {elapsed:.2f} s of compute; host has {os.cpu_count()} logical CPUs",
+            "attention_ms_per_problem": round(elapsed / done * 1e3, 2),
+            "append_ms": round(append_ms, 3), "euler_ms": round(euler_ms, 3), "blas": blas}
 
 
 def roofline(w, attn_ms: list) -> dict:
@@ -174,12 +196,7 @@ def cpu_baseline_prefill(w, budget_s: float):
 
     import oracle as O
     from workloads import gen as G
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - informational only
-        threads = os.cpu_count() or 1
+    threads, blas = blas_info()
     ids = G.history_unit_ids(w)
     kend = w.unit_kend()
     done, flops, elapsed = 0, 0, 0.0
@@ -200,7 +217,8 @@ def cpu_baseline_prefill(w, budget_s: float):
             "sample": f"fp64 NumPy oracle on {done} of {w.cached_units * w.heads} (head, unit) "
                       f"problems of this call (one unit's {w.video_tokens} queries over the cache "
                       f"up to its end, largest first), {elapsed:.2f} s of compute; host has "
-                      f"{os.cpu_count()} logical CPUs"}
+                      f"{os.cpu_count()} logical CPUs",
+            "attention_ms_per_problem": round(elapsed / done * 1e3, 2), "blas": blas}
 
 
 def prefill_bench(w, args) -> None:
