@@ -11,7 +11,6 @@ masked, straddling a unit boundary, and query tiles holding two units.
 """
 import numpy as np
 import pytest
-import torch
 
 import oracle as O
 import workloads as W
