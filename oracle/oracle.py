@@ -55,7 +55,10 @@ def bf16_to_f64(bits) -> np.ndarray:
 # -------------------------------------------------------------- cache append
 
 def kv_append(cache_k, cache_v, length, k_src, v_src, head_begin, layout=TOKEN_MAJOR):
-    """Write this rank's heads of one K/V slice into its local cache.
+    """Write this rank's heads of one K/V slice into its local cache
+    ("Wan-Streamer v0.2：更高分辨率，相同延迟" (structured summary), 前置知识
+    K/V缓存预分片 and 方法步骤详情: the rank writes its part of the slice straight
+    into its pre-split cache positions).
 
     cache_k, cache_v: uint16 bf16 bits [Hr][capacity][D] (not modified).
     k_src, v_src: uint16 bits, [n][H][D] (TOKEN_MAJOR) or [H][n][D] (HEAD_MAJOR).
@@ -94,7 +97,9 @@ def kv_append(cache_k, cache_v, length, k_src, v_src, head_begin, layout=TOKEN_M
 # ---------------------------------------------------- block-causal attention
 
 def visible(q_unit, k_unit) -> np.ndarray:
-    """Boolean [Nq][Nk]: key j is visible to query i iff unit(j) <= unit(i)."""
+    """Boolean [Nq][Nk]: key j is visible to query i iff unit(j) <= unit(i)
+    ("通义实验室发布 Wan-Streamer v0.2…" (remio.ai), 为什么端到端模型对级联式 AI 智能体构成挑战:
+    a block uses only what is available when it is produced)."""
     q_unit = np.asarray(q_unit, dtype=np.int64)
     k_unit = np.asarray(k_unit, dtype=np.int64)
     return k_unit[None, :] <= q_unit[:, None]
@@ -102,6 +107,7 @@ def visible(q_unit, k_unit) -> np.ndarray:
 
 def attention_probs_head(q, k, q_unit, k_unit, scale) -> np.ndarray:
     """Softmax weights of one head, float64 [Nq][Nk]; masked entries are 0.
+    The textbook softmax over the visible keys of visible().
 
     q: [Nq][D], k: [Nk][D] float64.
     """
@@ -118,7 +124,9 @@ def attention_probs_head(q, k, q_unit, k_unit, scale) -> np.ndarray:
 
 
 def attention(q, k, v, q_unit, k_unit, scale, row_chunk_elems=1 << 25) -> np.ndarray:
-    """Block-causal softmax attention, float64.
+    """Block-causal softmax attention, float64 ("通义实验室发布 Wan-Streamer v0.2…" (remio.ai), 为什么端到端模型对级联式 AI 智能体构成挑战;
+    "Wan-Streamer v0.2：更高分辨率，相同延迟" (structured summary), 方法步骤详情: each rank attends with its
+    local full-history cache).
 
     q: [H][Nq][D], k and v: [H][Nk][D] (float64 or bf16 bits as uint16);
     q_unit: [Nq] unit of each query; k_unit: [Nk] unit of each key (taken
@@ -151,7 +159,9 @@ def attention(q, k, v, q_unit, k_unit, scale, row_chunk_elems=1 << 25) -> np.nda
 
 def streaming_keys(cache_k, cache_v, length, cache_unit, k_self, v_self, self_unit):
     """Keys of a denoise step: valid cache rows [0, length) then the unit's own
-    tokens. Returns (k [H][Nk][D], v, k_unit [Nk]) as float64 / int64."""
+    tokens, which belong to the unit itself (the cache holds the full history:
+    "Wan-Streamer v0.2：更高分辨率，相同延迟" (structured summary), 方法步骤详情).
+    Returns (k [H][Nk][D], v, k_unit [Nk]) as float64 / int64."""
     ck = _as_f64(np.asarray(cache_k)[:, :length])
     cv = _as_f64(np.asarray(cache_v)[:, :length])
     cu = np.asarray(cache_unit, dtype=np.int64)[:length]
@@ -169,7 +179,9 @@ def streaming_keys(cache_k, cache_v, length, cache_unit, k_self, v_self, self_un
 # ------------------------------------------------------ flow-matching Euler
 
 def fm_euler_step(x, v_bits, dt) -> np.ndarray:
-    """One explicit Euler step x + dt * v in float64 from float32 x and bf16 v.
+    """One explicit Euler step x + dt * v in float64 from float32 x and bf16 v
+    ("Wan-Streamer v0.2：更高分辨率，相同延迟" (structured summary), 核心方法 and Thinker-Performer架构:
+    the performer generates the next unit's latent by flow matching).
 
     dt * v is exact in float64 (at most 24 + 8 significant bits), so the only
     rounding is that of the sum; the float32 state of the next step is this
