@@ -92,6 +92,8 @@ RAGGED = [
     (64, 3, 1, 1, 0),
     (64, 2, 31, 63, 5),
     (128, 2, 33, 65, 0),
+    (128, 3, 32, 97, 3),     # the largest call of the narrow kernel
+    (64, 2, 32, 130, 0),
     (128, 1, 129, 0, 200),
     (64, 5, 300, 500, 77),
     (128, 3, 257, 1000, 129),
