@@ -54,5 +54,27 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+DEMO_SRC = os.path.join(PKG_DIR, "examples", "c_abi_demo.c")
+DEMO_PATH = os.path.join(PKG_DIR, "examples", "c_abi_demo")
+
+
+def build_demo(verbose: bool = False) -> str:
+    """Compile examples/c_abi_demo.c, a plain C99 caller of include/ws.h,
+    against libws.so and the HIP runtime (host code only: gcc, no hipcc)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, DEMO_SRC,
+           "-L", PKG_DIR, "-lws", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", DEMO_PATH]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or res.returncode != 0:
+        print(" ".join(cmd))
+        print(res.stdout + res.stderr)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed with exit code {res.returncode}")
+    return DEMO_PATH
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_demo(verbose=True))

@@ -137,3 +137,11 @@ def test_split_planning_is_host_only_and_sized(lib):
     assert lib.ws_attn_default_splits(10, 32, 128, 244772) == 102
     assert lib.ws_attn_default_splits(3, 1, 64, 200) == 1
     assert lib.ws_attn_default_splits(2000, 4, 128, 244772) == 1
+
+
+def test_c_abi_demo_compiles_as_c99():
+    """include/ws.h is a C header: the plain-C demo builds with gcc -std=c99
+    -Wall -Wextra against libws.so."""
+    from cached_block_causal_amd import build as b
+    path = b.build_demo()
+    assert os.path.exists(path)
