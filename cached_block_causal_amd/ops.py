@@ -135,15 +135,16 @@ class AttnCall:
             ctypes.c_float(self.scale), ctypes.c_int32(self.splits),
             _dev16(out, "out", tuple(q.shape)),
             ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
-            ctypes.c_size_t(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
-            _stream(q))
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()) if workspace is not None else 0)
 
+    # the stream is torch's current one at each call (so a call made under
+    # torch.cuda.stream(...) or inside graph capture lands on that stream)
     def run(self) -> torch.Tensor:
-        L.check(L.lib().ws_block_causal_attn(*self.args), "ws_block_causal_attn")
+        L.check(L.lib().ws_block_causal_attn(*self.args, _stream(self.q)), "ws_block_causal_attn")
         return self.out
 
     def partial(self) -> None:
-        L.check(L.lib().ws_attn_partial(*self.args), "ws_attn_partial")
+        L.check(L.lib().ws_attn_partial(*self.args, _stream(self.q)), "ws_attn_partial")
 
     def merge(self) -> torch.Tensor:
         ws = self.workspace
