@@ -103,10 +103,36 @@ def blas_info():
             f"{lib.get('internal_api', '?')} {lib.get('version', '')}".strip())
 
 
-def cpu_baseline(w, budget_s: float):
+# parity bar of attention outputs against the oracle (bf16 in, fp32 accumulate)
+PARITY_MAX_ABS = 2e-2
+PARITY_REL_FRO = 5e-3
+
+
+class _Parity:
+    """Worst error of GPU outputs against the oracle over the problems seen."""
+
+    def __init__(self):
+        self.n, self.max_abs, self.rel = 0, 0.0, 0.0
+
+    def add(self, got_f64, want):
+        import numpy as np
+        diff = got_f64 - want
+        self.n += 1
+        self.max_abs = max(self.max_abs, float(np.max(np.abs(diff))))
+        self.rel = max(self.rel, float(np.linalg.norm(diff) / max(np.linalg.norm(want), 1e-300)))
+
+    def report(self):
+        return {"problems": self.n, "max_abs": self.max_abs, "rel_fro": self.rel,
+                "bar": {"max_abs": PARITY_MAX_ABS, "rel_fro": PARITY_REL_FRO},
+                "within": self.max_abs <= PARITY_MAX_ABS and self.rel <= PARITY_REL_FRO}
+
+
+def cpu_baseline(w, budget_s: float, gpu_out=None):
     """Time the fp64 oracle on a bounded sample of the same workload: whole
     (denoise step, head) attention problems (all query rows over all keys),
-    in step-then-head order, until about budget_s seconds of CPU time."""
+    in step-then-head order, until about budget_s seconds of CPU time.
+    gpu_out[step] (host bf16 bits [heads][n_q][D] of the timed run), when
+    given, is compared with each problem's oracle result outside the timing."""
     import numpy as np
 
     import oracle as O
@@ -114,6 +140,7 @@ def cpu_baseline(w, budget_s: float):
     threads, blas = blas_info()
     ids = G.history_unit_ids(w)
     done, flops, elapsed = 0, 0, 0.0
+    parity = _Parity()
     hist = {}
     for step in range(w.steps):
         for h in range(w.heads):
@@ -128,10 +155,12 @@ def cpu_baseline(w, budget_s: float):
             if w.joint:   # audio rows and keys first; video queries also see the audio tokens
                 ku[w.cache_len + w.audio_tokens:] += 1
                 qu[w.audio_tokens:] += 1
-            O.attention(q, k, v, qu, ku, 1 / np.sqrt(w.head_dim))
+            o = O.attention(q, k, v, qu, ku, 1 / np.sqrt(w.head_dim))
             elapsed += time.perf_counter() - t0
             done += 1
             flops += 4 * w.head_dim * w.visible_pairs()
+            if gpu_out is not None:
+                parity.add(O.bf16_to_f64(gpu_out[step][h]), o[0])
             if elapsed >= budget_s:
                 break
         if elapsed >= budget_s:
@@ -154,7 +183,8 @@ def cpu_baseline(w, budget_s: float):
                       f"attention problems of this workload ({w.n_q} queries x {w.n_keys} keys "
                       f"each), {elapsed:.2f} s of compute; host has {os.cpu_count()} logical CPUs",
             "attention_ms_per_problem": round(elapsed / done * 1e3, 2),
-            "append_ms": round(append_ms, 3), "euler_ms": round(euler_ms, 3), "blas": blas}
+            "append_ms": round(append_ms, 3), "euler_ms": round(euler_ms, 3), "blas": blas,
+            **({"parity": parity.report()} if gpu_out is not None else {})}
 
 
 def roofline(w, attn_ms: list) -> dict:
@@ -188,10 +218,12 @@ def roofline(w, attn_ms: list) -> dict:
     return r
 
 
-def cpu_baseline_prefill(w, budget_s: float):
+def cpu_baseline_prefill(w, budget_s: float, gpu_out=None):
     """The fp64 oracle on (head, unit) problems of the multi-unit call: the
     queries of one unit over the cache up to that unit's end, the largest
-    units first, until about budget_s seconds of CPU time."""
+    units first, until about budget_s seconds of CPU time. gpu_out (host
+    bf16 bits [heads][n_q][D] of the timed call), when given, is compared
+    with each problem's oracle result outside the timing."""
     import numpy as np
 
     import oracle as O
@@ -202,13 +234,17 @@ def cpu_baseline_prefill(w, budget_s: float):
     done, flops, elapsed = 0, 0, 0.0
     head = [w.head_begin]
     hk, hv = G.history_bits(w, head)
+    qb = w.q_unit_begin()
+    parity = _Parity()
     for u in reversed(range(w.cached_units)):
         q = G.prefill_queries(w, head, units=[u])
         t0 = time.perf_counter()
-        O.attention(q, hk[:, :kend[u]], hv[:, :kend[u]], np.full(w.video_tokens, u), ids[:kend[u]],
-                    1 / np.sqrt(w.head_dim))
+        o = O.attention(q, hk[:, :kend[u]], hv[:, :kend[u]], np.full(w.video_tokens, u),
+                        ids[:kend[u]], 1 / np.sqrt(w.head_dim))
         elapsed += time.perf_counter() - t0
         done += 1
+        if gpu_out is not None:
+            parity.add(O.bf16_to_f64(gpu_out[0, qb[u]:qb[u + 1]]), o[0])
         flops += 4 * w.head_dim * w.video_tokens * kend[u]
         if elapsed >= budget_s:
             break
@@ -218,7 +254,8 @@ def cpu_baseline_prefill(w, budget_s: float):
                       f"problems of this call (one unit's {w.video_tokens} queries over the cache "
                       f"up to its end, largest first), {elapsed:.2f} s of compute; host has "
                       f"{os.cpu_count()} logical CPUs",
-            "attention_ms_per_problem": round(elapsed / done * 1e3, 2), "blas": blas}
+            "attention_ms_per_problem": round(elapsed / done * 1e3, 2), "blas": blas,
+            **({"parity": parity.report()} if gpu_out is not None else {})}
 
 
 def prefill_bench(w, args) -> None:
@@ -228,7 +265,7 @@ def prefill_bench(w, args) -> None:
 
     from cached_block_causal_amd import AttnCall, KVCache, kv_append
     from workloads import gen as G
-    from workloads.device import dev_bits
+    from workloads.device import dev_bits, host_bits
     heads = list(range(w.head_begin, w.head_begin + w.heads))
     t_setup = time.perf_counter()
     cache = KVCache(w.heads, w.head_dim, w.capacity)
@@ -276,7 +313,7 @@ def prefill_bench(w, args) -> None:
         "setup_s": round(setup_s, 2),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds, host_bits(call.out))
     print(json.dumps(out), flush=True)
 
 
@@ -443,7 +480,7 @@ def main():
     import workloads as W
     from cached_block_causal_amd import AttnCall, KVCache, fm_euler_step, kv_append
     from workloads import gen as G
-    from workloads.device import dev_bits
+    from workloads.device import dev_bits, host_bits
 
     if args.calib_copy:
         calib_copy(args.steps)
@@ -577,7 +614,7 @@ def main():
                                    "denoise step, attention time = both partial launches"}
     out["graph"] = graph_replay(unit_step, args.steps)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, [host_bits(c.out) for c in calls])
     print(json.dumps(out), flush=True)
 
 
