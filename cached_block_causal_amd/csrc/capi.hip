@@ -60,7 +60,7 @@ constexpr int kMaxSplits = 256;
 
 int32_t default_splits(int32_t heads, int32_t n_q, int32_t head_dim, int64_t n_keys) {
   if (heads <= 0 || n_q <= 0 || n_keys <= 0 || head_dim <= 0) return 1;
-  const int64_t items = (int64_t)heads * ((n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM);
+  const int64_t items = (int64_t)heads * (((int64_t)n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM);
   const bool narrow = ws::attn_narrow(n_q);
   const int64_t tiles = (n_keys + (narrow ? ws::kAttnNarrowN : ws::kAttnBlockN) - 1) /
                         (narrow ? ws::kAttnNarrowN : ws::kAttnBlockN);
@@ -153,7 +153,7 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
   if (!aligned16(q) || !aligned16(out) || !aligned16(cache->k) || !aligned16(cache->v) ||
       !aligned16(k_self) || !aligned16(v_self))
     return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");
-  const int64_t n_qtiles = (n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM;
+  const int64_t n_qtiles = ((int64_t)n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM;
   const int64_t items = (int64_t)cache->heads * n_qtiles * splits;
   if (items > 0x7FFFFFF0) return fail(WS_ERR_SHAPE, "too many work items");
   if (splits > 1) {
@@ -308,7 +308,12 @@ ws_status ws_fm_euler_step(float* x, const void* v, int64_t n, float dt, void* s
 }
 
 const char* ws_status_string(ws_status s) {
-  switch (s) {
+  // A C caller may pass any int; read the bits as an int so that a value
+  // outside the enumerators is handled rather than loaded as the enum.
+  static_assert(sizeof(ws_status) == sizeof(int), "ws_status is passed as an int");
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case WS_OK: return "ok";
     case WS_ERR_NULL: return "null pointer";
     case WS_ERR_SHAPE: return "invalid size or table";

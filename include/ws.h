@@ -192,7 +192,7 @@ ws_status ws_attn_merge(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_
  */
 ws_status ws_fm_euler_step(float* x, const void* v, int64_t n, float dt, void* stream);
 
-/* Static text for a status code. */
+/* Static text for a status code ("unknown status" for any other value). */
 const char* ws_status_string(ws_status s);
 
 /* Detail of the last failing call on this thread ("" if none). Valid until

@@ -145,3 +145,36 @@ def test_c_abi_demo_compiles_as_c99():
     from cached_block_causal_amd import build as b
     path = b.build_demo()
     assert os.path.exists(path)
+
+
+def test_host_code_clean_under_asan_and_ubsan(tmp_path):
+    """The library's host code (argument validation, split planning, status
+    text) called from C under AddressSanitizer and UndefinedBehaviorSanitizer:
+    tests/capi_errors.c makes every refused call and runs the planning
+    functions over extreme sizes; neither sanitizer may report anything.
+    The sanitizers instrument host code only (no call reaches a GPU)."""
+    import subprocess
+    from cached_block_causal_amd import build as b
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(b.hipcc())))
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        pytest.skip("ROCm clang not found")
+    lib = str(tmp_path / "libws.so")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    r = subprocess.run([b.hipcc(), f"--offload-arch={b.ARCH}", "-O1", "-g", "-std=c++17", "-fPIC",
+                        "-shared", *san, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                        "-I", b.INCLUDE, "-I", b.CSRC, *[os.path.join(b.CSRC, s) for s in b.SOURCES],
+                        "-o", lib], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    exe = str(tmp_path / "capi_errors")
+    r = subprocess.run([clang, "-std=c99", "-O1", "-g", "-fsanitize=address,undefined",
+                        "-fno-omit-frame-pointer", "-I", b.INCLUDE,
+                        os.path.join(ROOT, "tests", "capi_errors.c"), lib,
+                        f"-Wl,-rpath,{tmp_path}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}",
+                        "-o", exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1",
+               ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0 and "capi_errors ok" in r.stdout, r.stdout + r.stderr[-3000:]
