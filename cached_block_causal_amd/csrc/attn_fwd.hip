@@ -714,11 +714,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   const int row = blockIdx.x * kRpb + row_in_block;
   const bool live = row < rows;
   float mx = kNegInf;
+  // (the split loops are unrolled so that several independent loads are in
+  // flight per thread)
   if (live)
+#pragma unroll 4
     for (int s = g; s < n_splits; s += G) mx = fmaxf(mx, part_lse[(int64_t)s * rows + row]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (live)
+#pragma unroll 4
     for (int s = g; s < n_splits; s += G) {
       const float lse = part_lse[(int64_t)s * rows + row];
       const float wgt = lse == kNegInf ? 0.f : fast_exp2(lse - mx);
