@@ -77,11 +77,35 @@ struct Tile {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Visible-key count of a query row from the unit table.
+// Visible-key count of a query row from the unit table: the key end of the
+// last unit that starts at or before the row. kTable: the table is in device
+// memory (a binary search; its row begins increase strictly), else in the
+// launch arguments. The two are separate kernel instances, so the common
+// in-argument case carries no code for the other.
+template <bool kTable>
 __device__ __forceinline__ int row_kend(const AttnArgs& a, int row) {
+  if constexpr (kTable) {
+    int lo = 0, hi = a.n_units - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.unit_table[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    return a.unit_table[a.n_units + 1 + lo];
+  }
   int u = 0;
   while (u + 1 < a.n_units && a.q_unit_begin[u + 1] <= row) ++u;
   return a.unit_kend[u];
+}
+// The same for every lane's own row (0 for rows past n_q); with the table in
+// the arguments the loop index is uniform, so it is read with scalar loads.
+template <bool kTable>
+__device__ __forceinline__ int lane_kend(const AttnArgs& a, int qrow) {
+  if (qrow >= a.n_q) return 0;
+  if constexpr (kTable) return row_kend<true>(a, qrow);
+  int kend = 0;
+  for (int u = 0; u < a.n_units; ++u) kend = qrow >= a.q_unit_begin[u] ? a.unit_kend[u] : kend;
+  return kend;
 }
 
 // Column group G (byte offset G*64 within each row, passed as the scalar
@@ -112,7 +136,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D>
+template <int D, bool kTable>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArgs a) {
   using T = Tile<D>;
   // separate objects per stage, so memory dependences between the in-flight
@@ -141,8 +165,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
 
   const int r0 = qt * kAttnBlockM;
   const int r_last = min(r0 + kAttnBlockM, a.n_q) - 1;
-  const int kmin = row_kend(a, r0);     // smallest visible range in this tile
-  const int kmax = row_kend(a, r_last);  // largest (kend is non-decreasing)
+  const int kmin = row_kend<kTable>(a, r0);     // smallest visible range in this tile
+  const int kmax = row_kend<kTable>(a, r_last);  // largest (kend is non-decreasing)
   // tiles: cache rows [0, min(len, kmax)) then own tokens [len, kmax)
   const int cache_rows = min(a.len, kmax);
   const int self_rows = max(0, kmax - a.len);
@@ -159,11 +183,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   // ---- this lane's query row and its Q^T operands
   const int qrow = r0 + wave * 32 + lrow;
   const bool wave_active = r0 + wave * 32 < a.n_q;
-  // the unit of a row is the last non-empty unit starting at or before it;
-  // the loop index is uniform, so the table is read with scalar loads
-  int kend = 0;
-  for (int u = 0; u < a.n_units; ++u) kend = qrow >= a.q_unit_begin[u] ? a.unit_kend[u] : kend;
-  if (qrow >= a.n_q) kend = 0;
+  // the unit of a row is the last non-empty unit starting at or before it
+  const int kend = lane_kend<kTable>(a, qrow);
   u32x4 qf[T::kDSteps];
   {
     const uint16_t* qp = a.q + ((int64_t)h * a.n_q + qrow) * D + 8 * half;
@@ -222,10 +243,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     const int local = (own ? t - n_ct : t) * kAttnBlockN;
     TileLoc L;
     L.abs_base = own ? a.len + local : local;
-    // rows <= 0 past the end of the split: an empty range, loads read zeros.
+    // tiles r >= n_t (past the split's end) are empty ranges: their loads
+    // read zeros and move nothing, and their scores are masked entirely.
     // (The clamp would otherwise become a VALU med3, making the resource look
     // per-lane and every load a waterfall loop.)
-    L.rows = __builtin_amdgcn_readfirstlane(max(0, min(kAttnBlockN, (own ? self_rows : cache_rows) - local)));
+    L.rows = __builtin_amdgcn_readfirstlane(
+        r < n_t ? max(0, min(kAttnBlockN, (own ? self_rows : cache_rows) - local)) : 0);
     L.k = (own ? ks_h : kc_h) + (int64_t)local * D;
     L.v = (own ? vs_h : vc_h) + (int64_t)local * D;
     return L;
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
 // each at D = 128) with no barrier, and per tile computes S^T (8 MFMAs at
 // D = 128), the softmax of 16 scores per lane and O^T += V^T P^T (8 MFMAs).
 // Partials go through the same workspace and merge as the main kernel's.
-template <int D>
+template <int D, bool kTable>
 __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   using T = Tile<D>;
   constexpr int kN = kAttnNarrowN;            // keys per tile
@@ -506,8 +529,8 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   const int lrow = lane & 31;
   const int half = lane >> 5;
 
-  const int kmin = row_kend(a, 0);
-  const int kmax = row_kend(a, a.n_q - 1);
+  const int kmin = row_kend<kTable>(a, 0);
+  const int kmax = row_kend<kTable>(a, a.n_q - 1);
   const int cache_rows = min(a.len, kmax);
   const int self_rows = max(0, kmax - a.len);
   const int n_ct = (cache_rows + kN - 1) / kN;
@@ -521,9 +544,7 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   const uint16_t* vs_h = a.vs + (int64_t)h * a.n_self * D;
 
   const int qrow = lrow;
-  int kend = 0;
-  for (int u = 0; u < a.n_units; ++u) kend = qrow >= a.q_unit_begin[u] ? a.unit_kend[u] : kend;
-  if (qrow >= a.n_q) kend = 0;
+  const int kend = lane_kend<kTable>(a, qrow);
   u32x4 qf[T::kDSteps];
   {
     const uint16_t* qp = a.q + ((int64_t)h * a.n_q + qrow) * D + 8 * half;
@@ -760,22 +781,51 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
       u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
 }
 
+constexpr int kTableChunk = 896;  // ints per launch (3.6 KB of arguments)
+struct TableChunk {
+  int* dst;
+  int n;
+  int v[kTableChunk];
+};
+__global__ __launch_bounds__(256) void unit_table_kernel(const TableChunk c) {
+  for (int i = threadIdx.x; i < c.n; i += 256) c.dst[i] = c.v[i];
+}
+
 }  // namespace
 
-hipError_t launch_attn_partial(const AttnArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_unit_table(int* dst, const int* vals, int n, hipStream_t stream) {
+  for (int b = 0; b < n; b += kTableChunk) {
+    TableChunk c;
+    c.dst = dst + b;
+    c.n = n - b < kTableChunk ? n - b : kTableChunk;
+    for (int i = 0; i < c.n; ++i) c.v[i] = vals[b + i];
+    hipLaunchKernelGGL(unit_table_kernel, dim3(1), dim3(256), 0, stream, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <bool kTable>
+hipError_t launch_attn_partial_t(const AttnArgs& a, int head_dim, hipStream_t stream) {
   if (attn_narrow(a.n_q)) {
     if (head_dim == 128)
-      hipLaunchKernelGGL(attn_narrow_kernel<128>, dim3(a.n_items), dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((attn_narrow_kernel<128, kTable>), dim3(a.n_items), dim3(64), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_narrow_kernel<64>, dim3(a.n_items), dim3(64), 0, stream, a);
+      hipLaunchKernelGGL((attn_narrow_kernel<64, kTable>), dim3(a.n_items), dim3(64), 0, stream, a);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((a.n_items + 7) / 8 * 8);
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_partial_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_kernel<128, kTable>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_partial_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attn_partial_kernel<64, kTable>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_partial(const AttnArgs& a, int head_dim, hipStream_t stream) {
+  return a.unit_table ? launch_attn_partial_t<true>(a, head_dim, stream)
+                      : launch_attn_partial_t<false>(a, head_dim, stream);
 }
 
 hipError_t launch_attn_merge(const float* part_o, const float* part_lse, uint16_t* out,

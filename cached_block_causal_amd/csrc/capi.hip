@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "ws.h"
 #include "ws_launch.hpp"
@@ -97,15 +98,41 @@ size_t lse_offset(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits
   return (o + 255) & ~(size_t)255;
 }
 
+// Workspace: split partials [S][heads][n_q][D] floats and their log2-sum-
+// exps [S][heads][n_q] (S > 1), then, for calls of more than WS_MAX_UNITS
+// queries, room for a unit table of up to n_q non-empty units
+// ([n + 1] row begins, [n] key ends), each region 256-byte aligned.
+size_t table_offset(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits) {
+  if (n_splits <= 1) return 0;
+  const size_t e = lse_offset(heads, n_q, head_dim, n_splits) + (size_t)n_splits * heads * n_q * sizeof(float);
+  return (e + 255) & ~(size_t)255;
+}
+
 size_t workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits) {
-  if (heads <= 0 || n_q <= 0 || head_dim <= 0 || n_splits <= 1) return 0;
-  return lse_offset(heads, n_q, head_dim, n_splits) + (size_t)n_splits * heads * n_q * sizeof(float);
+  if (heads <= 0 || n_q <= 0 || head_dim <= 0 || n_splits <= 0) return 0;
+  const size_t table = n_q > WS_MAX_UNITS ? (2 * (size_t)n_q + 1) * sizeof(int32_t) : 0;
+  if (n_splits <= 1) return table;
+  return table ? table_offset(heads, n_q, head_dim, n_splits) + table
+               : lse_offset(heads, n_q, head_dim, n_splits) +
+                     (size_t)n_splits * heads * n_q * sizeof(float);
 }
 
 struct AttnPlan {
   ws::AttnArgs args;
   int32_t splits;
+  std::vector<int> table;  // unit table to copy to args.unit_table before the pass
 };
+
+// Enqueue the unit-table copy (if any), then the split-KV pass.
+ws_status launch_partial(const AttnPlan& plan, int32_t head_dim, hipStream_t s) {
+  if (!plan.table.empty()) {
+    ws_status st = hip_status(ws::launch_unit_table(const_cast<int*>(plan.args.unit_table),
+                                                    plan.table.data(), (int)plan.table.size(), s),
+                              "unit table launch");
+    if (st != WS_OK) return st;
+  }
+  return hip_status(ws::launch_attn_partial(plan.args, head_dim, s), "attention launch");
+}
 
 // Validate a ws_block_causal_attn / ws_attn_partial call and fill the kernel
 // arguments. Returns WS_OK with plan->splits == 0 for a no-op (n_q == 0).
@@ -119,8 +146,6 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
   if (n_q < 0) return fail(WS_ERR_SHAPE, "n_q %d < 0", n_q);
   if (n_self < 0) return fail(WS_ERR_SHAPE, "n_self %d < 0", n_self);
   if (n_units < 1) return fail(WS_ERR_SHAPE, "n_units %d < 1", n_units);
-  if (n_units > WS_MAX_UNITS)
-    return fail(WS_ERR_UNSUPPORTED, "n_units %d > %d", n_units, WS_MAX_UNITS);
   if (!q_unit_begin || !unit_kend) return fail(WS_ERR_NULL, "unit table is NULL");
   if (q_unit_begin[0] != 0) return fail(WS_ERR_SHAPE, "q_unit_begin[0] = %d != 0", q_unit_begin[0]);
   for (int32_t u = 0; u < n_units; ++u)
@@ -143,6 +168,9 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
     return fail(WS_ERR_SHAPE, "n_splits %d outside [0, %d]", n_splits, kMaxSplits);
   const int32_t d = cache->head_dim;
   const int32_t splits = n_splits ? n_splits : default_splits(cache->heads, n_q, d, n_keys);
+  // units with at least one query row; the others change no row's keys
+  int32_t n_live = 0;
+  for (int32_t u = 0; u < n_units; ++u) n_live += q_unit_begin[u + 1] > q_unit_begin[u];
   if (n_q == 0) {
     plan->splits = 0;
     return WS_OK;
@@ -156,8 +184,12 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
   const int64_t n_qtiles = ((int64_t)n_q + ws::kAttnBlockM - 1) / ws::kAttnBlockM;
   const int64_t items = (int64_t)cache->heads * n_qtiles * splits;
   if (items > 0x7FFFFFF0) return fail(WS_ERR_SHAPE, "too many work items");
-  if (splits > 1) {
-    const size_t need = workspace_bytes(cache->heads, n_q, d, splits);
+  if (splits > 1 || n_live > WS_MAX_UNITS) {
+    // what this call writes: the partials, and the unit table if it has one
+    const size_t need =
+        n_live > WS_MAX_UNITS
+            ? table_offset(cache->heads, n_q, d, splits) + (2 * (size_t)n_live + 1) * sizeof(int32_t)
+            : lse_offset(cache->heads, n_q, d, splits) + (size_t)splits * cache->heads * n_q * sizeof(float);
     if (!workspace) return fail(WS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes_in < need)
       return fail(WS_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes_in, need);
@@ -185,9 +217,29 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
   a.n_qtiles = (int)n_qtiles;
   a.n_items = (int)items;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.n_units = n_units;
-  for (int32_t u = 0; u <= n_units; ++u) a.q_unit_begin[u] = q_unit_begin[u];
-  for (int32_t u = 0; u < n_units; ++u) a.unit_kend[u] = unit_kend[u];
+  a.n_units = n_live;
+  plan->table.clear();
+  if (n_live <= WS_MAX_UNITS) {
+    int32_t i = 0;
+    for (int32_t u = 0; u < n_units; ++u) {
+      if (q_unit_begin[u + 1] == q_unit_begin[u]) continue;
+      a.q_unit_begin[i] = q_unit_begin[u];
+      a.unit_kend[i++] = unit_kend[u];
+    }
+    a.q_unit_begin[n_live] = n_q;
+  } else {
+    std::vector<int>& t = plan->table;
+    t.resize(2 * (size_t)n_live + 1);
+    int32_t i = 0;
+    for (int32_t u = 0; u < n_units; ++u) {
+      if (q_unit_begin[u + 1] == q_unit_begin[u]) continue;
+      t[i] = q_unit_begin[u];
+      t[n_live + 1 + i++] = unit_kend[u];
+    }
+    t[n_live] = n_q;
+    a.unit_table = reinterpret_cast<const int*>(static_cast<char*>(workspace) +
+                                                table_offset(cache->heads, n_q, d, splits));
+  }
   plan->splits = splits;
   return WS_OK;
 }
@@ -247,9 +299,7 @@ ws_status ws_attn_partial(const ws_kv_cache* cache, const void* q, int32_t n_q, 
   ws_status st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend,
                            scale, n_splits, out, workspace, workspace_bytes_in, &plan);
   if (st != WS_OK || plan.splits == 0) return st;
-  return hip_status(ws::launch_attn_partial(plan.args, cache->head_dim,
-                                            static_cast<hipStream_t>(stream)),
-                    "attention launch");
+  return launch_partial(plan, cache->head_dim, static_cast<hipStream_t>(stream));
 }
 
 ws_status ws_attn_merge(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_splits,
@@ -288,7 +338,7 @@ ws_status ws_block_causal_attn(const ws_kv_cache* cache, const void* q, int32_t 
                            scale, n_splits, out, workspace, workspace_bytes_in, &plan);
   if (st != WS_OK || plan.splits == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(ws::launch_attn_partial(plan.args, cache->head_dim, s), "attention launch");
+  st = launch_partial(plan, cache->head_dim, s);
   if (st != WS_OK || plan.splits == 1) return st;
   return hip_status(ws::launch_attn_merge(plan.args.part_o, plan.args.part_lse, plan.args.out,
                                           cache->heads, n_q, cache->head_dim, plan.splits, s),

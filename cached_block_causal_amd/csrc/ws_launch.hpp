@@ -31,10 +31,19 @@ struct AttnArgs {
   int heads, n_q, len, n_self;
   int n_splits, n_qtiles, n_items;
   float scale_log2;         // softmax scale * log2(e)
+  // Units with at least one query row (empty units change no row's keys).
+  // Up to WS_MAX_UNITS of them travel here; a call with more keeps its table
+  // in device memory: unit_table = [n_units + 1 row begins][n_units key ends].
   int n_units;
   int q_unit_begin[WS_MAX_UNITS + 1];
   int unit_kend[WS_MAX_UNITS];
+  const int* unit_table;
 };
+
+// Copy a host int table to device memory with kernel launches whose
+// arguments carry the values (no host-side staging buffer, and the same under
+// graph capture).
+hipError_t launch_unit_table(int* dst, const int* vals, int n, hipStream_t stream);
 
 // Rows of queries one workgroup of the split-KV pass covers.
 constexpr int kAttnBlockM = 128;

@@ -50,7 +50,7 @@ typedef enum ws_status {
   WS_ERR_SHAPE = 2,        /* a size, index or unit table is out of range        */
   WS_ERR_CAPACITY = 3,     /* an append would overflow the cache                 */
   WS_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned            */
-  WS_ERR_UNSUPPORTED = 5,  /* head_dim not 64/128, too many units, bad layout    */
+  WS_ERR_UNSUPPORTED = 5,  /* head_dim not 64/128, or an unknown source layout   */
   WS_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required         */
   WS_ERR_HIP = 7           /* the HIP runtime refused a launch                   */
 } ws_status;
@@ -61,7 +61,8 @@ enum {
   WS_HEAD_MAJOR = 1        /* [src_heads][n_tok][head_dim]: head-sharded latents  */
 };
 
-/* Most units one ws_block_causal_attn call may describe. */
+/* Units with queries whose table travels in the launch arguments. A call with
+   more keeps its unit table in the workspace (see ws_attn_workspace_bytes). */
 #define WS_MAX_UNITS 64
 
 /*
@@ -83,10 +84,10 @@ typedef struct ws_kv_cache {
 
 /*
  * ws_kv_append -- write this GPU's part of an incoming K/V slice straight into
- * its cache positions ([Summary] 前置知识, K/V缓存预分片 and 方法步骤详情: each
- * performer rank writes the thinker's new slice into its own pre-split local
- * cache; [Abstract]: each performer rank writes incoming K/V into a pre-sharded
- * local cache).
+ * its cache positions ([Summary] 前置知识, K/V缓存预分片 and 方法步骤详情;
+ * [Abstract]): a rank stores its own head block of every new slice in a
+ * cache that was split and allocated ahead of time, so the write itself
+ * moves nothing between GPUs.
  *
  *   For h in [0, cache->heads), t in [0, n_tok):
  *     cache->k[h][cache->len + t][:] = k_src[t][head_begin + h][:]   (WS_TOKEN_MAJOR)
@@ -109,8 +110,12 @@ ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src,
  * contiguous chunks processed by separate workgroups and merged by
  * log-sum-exp weights. ws_attn_default_splits returns the library's choice
  * (>= 1) for a call with these sizes; ws_attn_workspace_bytes returns the
- * workspace a call with n_splits needs (0 when n_splits == 1). Both are pure
- * host functions. Non-positive sizes give 1 and 0.
+ * workspace a call with n_splits needs: the split partials when n_splits >
+ * 1, plus, when n_q > WS_MAX_UNITS, room for a unit table of up to n_q units
+ * (a call with more than WS_MAX_UNITS units holding queries copies its table
+ * there with one small kernel launch per 896 entries). A call with one split
+ * and at most WS_MAX_UNITS units with queries needs none. Both are pure host
+ * functions. Non-positive sizes give 1 and 0.
  */
 int32_t ws_attn_default_splits(int32_t heads, int32_t n_q, int32_t head_dim,
                                int64_t n_keys);
@@ -137,7 +142,7 @@ size_t ws_attn_workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim,
  *
  *   q:   device bf16 [heads][n_q][head_dim]   (heads = cache->heads)
  *   k_self, v_self: device bf16 [heads][n_self][head_dim]; may be NULL if n_self == 0
- *   n_units in [1, WS_MAX_UNITS]; q_unit_begin: host int32[n_units + 1],
+ *   n_units >= 1; q_unit_begin: host int32[n_units + 1],
  *     q_unit_begin[0] == 0, non-decreasing, q_unit_begin[n_units] == n_q;
  *   unit_kend: host int32[n_units], non-decreasing, 1 <= unit_kend[u] <=
  *     cache->len + n_self.
@@ -147,8 +152,9 @@ size_t ws_attn_workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim,
  *     otherwise 1..256.
  *   out: device bf16 [heads][n_q][head_dim].
  *   workspace: device buffer of >= ws_attn_workspace_bytes(...) bytes when
- *     the split count used is > 1 (NULL allowed otherwise); overwritten.
- * Errors: WS_ERR_NULL, WS_ERR_SHAPE, WS_ERR_UNSUPPORTED (head_dim, n_units),
+ *     the split count used is > 1 or more than WS_MAX_UNITS units hold
+ *     queries (NULL allowed otherwise); overwritten.
+ * Errors: WS_ERR_NULL, WS_ERR_SHAPE, WS_ERR_UNSUPPORTED (head_dim),
  * WS_ERR_WORKSPACE, WS_ERR_ALIGN, WS_ERR_HIP. n_q == 0 is a no-op.
  */
 ws_status ws_block_causal_attn(const ws_kv_cache* cache,

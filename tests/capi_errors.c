@@ -51,7 +51,15 @@ int main(void) {
   expect("attn null q", ws_block_causal_attn(&c, NULL, 8, FAKE, FAKE, 2, 1, qb, ke, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_NULL);
   expect("attn null table", ws_block_causal_attn(&c, FAKE, 8, FAKE, FAKE, 2, 1, NULL, ke, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_NULL);
   expect("attn units 0", ws_block_causal_attn(&c, FAKE, 8, FAKE, FAKE, 2, 0, qb, ke, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_SHAPE);
-  expect("attn too many units", ws_block_causal_attn(&c, FAKE, 8, FAKE, FAKE, 2, WS_MAX_UNITS + 1, qb, ke, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_UNSUPPORTED);
+  {
+    /* more units with queries than the launch arguments hold: the table
+       goes to the workspace, which is then required */
+    int32_t qb70[71], ke70[70];
+    for (int u = 0; u <= 70; ++u) qb70[u] = u;
+    for (int u = 0; u < 70; ++u) ke70[u] = 1 + u / 10;
+    expect("attn many units, no workspace", ws_block_causal_attn(&c, FAKE, 70, FAKE, FAKE, 2, 70, qb70, ke70, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_WORKSPACE);
+    expect("attn many units, short workspace", ws_block_causal_attn(&c, FAKE, 70, FAKE, FAKE, 2, 70, qb70, ke70, 0.1f, 1, FAKE, FAKE2, 16, NULL), WS_ERR_WORKSPACE);
+  }
   ke[0] = 13;
   expect("attn kend past keys", ws_block_causal_attn(&c, FAKE, 8, FAKE, FAKE, 2, 1, qb, ke, 0.1f, 1, FAKE, NULL, 0, NULL), WS_ERR_SHAPE);
   ke[0] = 0;

@@ -93,7 +93,12 @@ def test_attention_validation(lib):
     assert _attn(lib, c, units=2, qb=[0, 30, 20], kend=[5, 10]) == L.WS_ERR_SHAPE
     assert _attn(lib, c, units=2, qb=[0, 20, 50], kend=[8, 5]) == L.WS_ERR_SHAPE
     assert _attn(lib, c, units=0) == L.WS_ERR_SHAPE
-    assert _attn(lib, c, units=65, qb=[0] * 65 + [50], kend=[10] * 65) == L.WS_ERR_UNSUPPORTED
+    # more than WS_MAX_UNITS units with queries: their table needs the workspace
+    live = list(range(71))
+    assert _attn(lib, c, nq=70, units=70, qb=live, kend=[10] * 70) == L.WS_ERR_WORKSPACE
+    assert _attn(lib, c, nq=70, units=70, qb=live, kend=[10] * 70, ws=FAKE,
+                 wsb=lib.ws_attn_workspace_bytes(2, 70, 128, 1) - 4) == L.WS_ERR_WORKSPACE
+    assert _attn(lib, c, nq=70, units=70, qb=live, kend=list(range(10, 0, -1)) * 7) == L.WS_ERR_SHAPE
     assert _attn(lib, c, scale=0.0) == L.WS_ERR_SHAPE
     assert _attn(lib, c, scale=float("nan")) == L.WS_ERR_SHAPE
     assert _attn(lib, c, splits=-1) == L.WS_ERR_SHAPE
@@ -124,13 +129,15 @@ def test_merge_and_euler_validation(lib):
 
 def test_split_planning_is_host_only_and_sized(lib):
     assert lib.ws_attn_default_splits(0, 10, 128, 100) == 1
-    assert lib.ws_attn_workspace_bytes(10, 920, 128, 1) == 0
+    # one split: nothing, or room for a unit table of up to n_q units
+    assert lib.ws_attn_workspace_bytes(10, 64, 128, 1) == 0
+    assert lib.ws_attn_workspace_bytes(10, 920, 128, 1) == (2 * 920 + 1) * 4
     for heads, nq, d, nk in [(10, 920, 128, 61880), (40, 920, 128, 61880), (24, 252, 128, 9372),
                              (40, 4, 128, 244772), (4, 252, 64, 804)]:
         s = lib.ws_attn_default_splits(heads, nq, d, nk)
         assert 1 <= s <= 256
         need = lib.ws_attn_workspace_bytes(heads, nq, d, s)
-        assert (s == 1 and need == 0) or need >= s * heads * nq * (d + 1) * 4
+        assert need >= (s > 1) * s * heads * nq * (d + 1) * 4 + (nq > 64) * (2 * nq + 1) * 4
     # at most 32 queries: one round of 1024 one-wave workgroups, at most a
     # quarter of the 32-key tiles per split
     assert lib.ws_attn_default_splits(40, 4, 128, 244772) == 25

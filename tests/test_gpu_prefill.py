@@ -104,3 +104,68 @@ def test_prefill_splits_agree_bitwise_per_split_count():
     want = O.attention(q, k, v, qu, ku, 1 / np.sqrt(128))
     for s, out in runs.items():
         assert_close(out, want, f"6 units splits {s}")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("n_splits", [0, 1])
+def test_256_units_audio_history_sampled_rows(n_splits):
+    """Re-encoding of a 256-unit audio-era history in one call (each unit of
+    956 keys; its 4 audio tokens as queries over the cache up to its own
+    end): more units than the launch arguments carry, so the unit table goes
+    through the workspace. Rows of the first, middle and last units and
+    random rows on three heads against the oracle; every output finite."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn, kv_append
+    unit_keys = [956] * 256
+    unit_queries = [4] * 256
+    k, v, q, ku, qu, qb, kend = _ragged_case(128, unit_keys, unit_queries, 17)
+    print(f"256 units: n_q {q.shape[1]} n_keys {k.shape[1]} splits {n_splits}", flush=True)
+    cache = poisoned_cache(3, 128, k.shape[1] + 64)
+    kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
+    out = host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=qb, unit_kend=kend,
+                                      n_splits=n_splits))
+    assert all_finite_bits(out)
+    rng = np.random.default_rng(3)
+    rows = sorted(set(list(range(8)) + list(range(512, 516)) + list(range(1016, 1024))
+                      + list(rng.integers(0, 1024, 24))))
+    rows = np.array(rows)
+    want = O.attention(q[:, rows], k, v, qu[rows], ku, 1 / np.sqrt(128))
+    print(assert_close(out[:, rows], want, f"256 units splits {n_splits}"), flush=True)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("n_splits", [0, 1, 3])
+def test_over_200_ragged_units_every_output(head_dim, n_splits):
+    """230 units of 1..40 keys and 0..6 queries (a quarter of them empty):
+    more than 64 units with queries, so the table is in device memory and
+    rows find their unit by binary search; every output against the oracle.
+    A second call with the same queries gathered into 40 units (the rest
+    empty) takes the in-argument table."""
+    need_gpu()
+    from cached_block_causal_amd import block_causal_attn, kv_append
+    rng = np.random.default_rng(23)
+    unit_keys = rng.integers(1, 41, 230).tolist()
+    unit_queries = rng.integers(0, 7, 230)
+    unit_queries[rng.random(230) < 0.25] = 0
+    unit_queries = unit_queries.tolist()
+    k, v, q, ku, qu, qb, kend = _ragged_case(head_dim, unit_keys, unit_queries, 29)
+    live = sum(1 for n in unit_queries if n)
+    print(f"{len(unit_keys)} units ({live} with queries) n_q {q.shape[1]} n_keys {k.shape[1]} "
+          f"D {head_dim} splits {n_splits}", flush=True)
+    assert live > 64
+    cache = poisoned_cache(3, head_dim, k.shape[1] + 5)
+    kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
+    out = host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=qb, unit_kend=kend,
+                                      n_splits=n_splits))
+    want = O.attention(q, k, v, qu, ku, 1 / np.sqrt(head_dim))
+    assert_close(out, want, f"230 units D {head_dim} splits {n_splits}")
+    # the same rows in at most 40 non-empty units: queries move to the last
+    # unit whose key end is <= their own, so each row sees fewer keys
+    keep = sorted(set(np.linspace(0, 229, 40).astype(int).tolist()))
+    unit_of = np.array([max(u for u in keep if u <= x) for x in qu])
+    uq2 = [int(np.sum(unit_of == u)) for u in range(230)]
+    qb2 = np.concatenate([[0], np.cumsum(uq2)]).tolist()
+    out2 = host_bits(block_causal_attn(cache, dev_bits(q), q_unit_begin=qb2, unit_kend=kend,
+                                       n_splits=n_splits))
+    want2 = O.attention(q, k, v, unit_of, ku, 1 / np.sqrt(head_dim))
+    assert_close(out2, want2, f"40 of 230 units D {head_dim} splits {n_splits}")
