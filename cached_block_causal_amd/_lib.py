@@ -19,6 +19,7 @@ WS_ERR_HIP = 7
 WS_TOKEN_MAJOR = 0
 WS_HEAD_MAJOR = 1
 WS_MAX_UNITS = 64
+WS_SCRATCH_BYTES = 32 << 20
 
 
 class WsKvCache(ctypes.Structure):
@@ -56,6 +57,11 @@ SIGNATURES = {
     "ws_attn_merge": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                      ctypes.c_void_p]),
+    "ws_block_causal_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(WsKvCache), ctypes.c_void_p,
+                                                    ctypes.c_int32, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                                    _I32P, _I32P, ctypes.c_float, ctypes.c_int32,
+                                                    ctypes.c_void_p, ctypes.c_void_p]),
     "ws_fm_euler_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_float, ctypes.c_void_p]),
     "ws_status_string": (ctypes.c_char_p, [ctypes.c_int]),

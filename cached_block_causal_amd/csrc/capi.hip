@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -115,6 +116,47 @@ size_t workspace_bytes(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_s
   return table ? table_offset(heads, n_q, head_dim, n_splits) + table
                : lse_offset(heads, n_q, head_dim, n_splits) +
                      (size_t)n_splits * heads * n_q * sizeof(float);
+}
+
+// Bytes of workspace a call writes: its split partials, or, when more than
+// WS_MAX_UNITS units hold queries, everything up to the end of its unit table.
+size_t attn_need_bytes(int32_t heads, int32_t n_q, int32_t head_dim, int32_t splits,
+                       int32_t n_live) {
+  if (n_live > WS_MAX_UNITS)
+    return table_offset(heads, n_q, head_dim, splits) + (2 * (size_t)n_live + 1) * sizeof(int32_t);
+  if (splits <= 1) return 0;
+  return lse_offset(heads, n_q, head_dim, splits) + (size_t)splits * heads * n_q * sizeof(float);
+}
+
+// ---- library-held scratch for callers that cannot allocate
+//
+// One array per GPU, alive until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address
+// is looked up once per device (that device current) and only that address
+// is passed to kernels.
+static __device__ __align__(256) char scratch[WS_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ws_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  ws_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != WS_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(WS_ERR_UNSUPPORTED, "device %d outside the %d the scratch table tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != WS_OK) return st;
+    if (!p) return fail(WS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WS_OK;
 }
 
 struct AttnPlan {
@@ -336,6 +378,56 @@ ws_status ws_block_causal_attn(const ws_kv_cache* cache, const void* q, int32_t 
   AttnPlan plan;
   ws_status st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend,
                            scale, n_splits, out, workspace, workspace_bytes_in, &plan);
+  if (st != WS_OK || plan.splits == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_partial(plan, cache->head_dim, s);
+  if (st != WS_OK || plan.splits == 1) return st;
+  return hip_status(ws::launch_attn_merge(plan.args.part_o, plan.args.part_lse, plan.args.out,
+                                          cache->heads, n_q, cache->head_dim, plan.splits, s),
+                    "merge launch");
+}
+
+ws_status ws_block_causal_attn_noalloc(const ws_kv_cache* cache, const void* q, int32_t n_q,
+                                       const void* k_self, const void* v_self, int32_t n_self,
+                                       int32_t n_units, const int32_t* q_unit_begin,
+                                       const int32_t* unit_kend, float scale, int32_t n_splits,
+                                       void* out, void* stream) {
+  g_last_error.clear();
+  // Size the call against the scratch before touching the GPU: the default
+  // split count is lowered until its partials fit; an explicit one that does
+  // not fit is refused.
+  int32_t splits = n_splits;
+  if (cache && q_unit_begin && n_units >= 1 && n_q > 0 && n_splits >= 0 &&
+      head_dim_ok(cache->head_dim) && cache->heads >= 1) {
+    int32_t n_live = 0;
+    for (int32_t u = 0; u < n_units; ++u) n_live += q_unit_begin[u + 1] > q_unit_begin[u];
+    const int64_t n_keys = (int64_t)cache->len + (n_self > 0 ? n_self : 0);
+    if (splits == 0) {
+      splits = default_splits(cache->heads, n_q, cache->head_dim, n_keys);
+      while (splits > 1 &&
+             attn_need_bytes(cache->heads, n_q, cache->head_dim, splits, n_live) > WS_SCRATCH_BYTES)
+        --splits;
+    }
+    const size_t need = attn_need_bytes(cache->heads, n_q, cache->head_dim, splits, n_live);
+    if (need > WS_SCRATCH_BYTES)
+      return fail(WS_ERR_WORKSPACE,
+                  "the call needs %zu bytes of scratch; the library holds %zu per GPU "
+                  "(use fewer splits or ws_block_causal_attn with a workspace)",
+                  need, (size_t)WS_SCRATCH_BYTES);
+  }
+  AttnPlan plan;
+  // validation first (also of the sizes above); the GPU is touched only for
+  // a call that will launch
+  ws_status st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend,
+                           scale, splits, out, nullptr, 0, &plan);
+  if (st == WS_ERR_WORKSPACE) {
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != WS_OK) return st;
+    g_last_error.clear();
+    st = plan_attn(cache, q, n_q, k_self, v_self, n_self, n_units, q_unit_begin, unit_kend, scale,
+                   splits, out, ws, WS_SCRATCH_BYTES, &plan);
+  }
   if (st != WS_OK || plan.splits == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_partial(plan, cache->head_dim, s);

@@ -163,6 +163,28 @@ def block_causal_attn(cache: KVCache, q, k_self=None, v_self=None, q_unit_begin=
                     out, workspace).run()
 
 
+def block_causal_attn_noalloc(cache: KVCache, q, k_self=None, v_self=None, q_unit_begin=None,
+                              unit_kend=None, scale=None, n_splits=0, out=None):
+    """ws_block_causal_attn_noalloc: no workspace; the library's per-GPU
+    scratch holds the split partials. Returns out."""
+    hr, d = cache.heads, cache.head_dim
+    if q.dim() != 3 or q.shape[0] != hr or q.shape[2] != d:
+        raise ValueError(f"q must be [{hr}][n_q][{d}]")
+    n_q = q.shape[1]
+    n_self = 0 if k_self is None else k_self.shape[1]
+    n_units, qb, ke = _units(n_q, cache.len + n_self, q_unit_begin, unit_kend)
+    if out is None:
+        out = torch.empty_like(q, dtype=torch.bfloat16)
+    st = L.lib().ws_block_causal_attn_noalloc(
+        ctypes.byref(cache.struct), _dev16(q, "q"), n_q,
+        _dev16(k_self, "k_self", (hr, n_self, d)) if k_self is not None else None,
+        _dev16(v_self, "v_self", (hr, n_self, d)) if v_self is not None else None,
+        n_self, n_units, qb, ke, ctypes.c_float(1.0 / math.sqrt(d) if scale is None else scale),
+        n_splits, _dev16(out, "out", tuple(q.shape)), _stream(q))
+    L.check(st, "ws_block_causal_attn_noalloc")
+    return out
+
+
 def fm_euler_step(x: torch.Tensor, v: torch.Tensor, dt: float) -> torch.Tensor:
     """ws_fm_euler_step: x (float32, in place) += dt * v (bf16)."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():

@@ -186,6 +186,32 @@ ws_status ws_attn_merge(int32_t heads, int32_t n_q, int32_t head_dim, int32_t n_
                         void* stream);
 
 /*
+ * ws_block_causal_attn_noalloc -- ws_block_causal_attn for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace. Its split partials and unit table live in scratch memory the
+ * library holds, WS_SCRATCH_BYTES per GPU (a static device array, alive
+ * until the process ends); the call allocates nothing.
+ *   - n_splits == 0: the default split count, lowered until the partials fit
+ *     the scratch; an explicit n_splits whose partials (or unit table) do not
+ *     fit is refused with WS_ERR_WORKSPACE before anything is enqueued.
+ *   - The scratch of a GPU is shared by every call on it and keeps the last
+ *     call's contents: two such calls that can run at the same time on one
+ *     GPU (different streams without ordering) race and give wrong results.
+ *     Calls on one stream, or ordered by events, are safe.
+ *   - The calling thread's current device must be the device of `stream`
+ *     (the scratch address is looked up per current device, once).
+ * Results equal ws_block_causal_attn's with the same split count.
+ */
+#define WS_SCRATCH_BYTES (32u << 20)
+ws_status ws_block_causal_attn_noalloc(const ws_kv_cache* cache,
+                                       const void* q, int32_t n_q,
+                                       const void* k_self, const void* v_self, int32_t n_self,
+                                       int32_t n_units, const int32_t* q_unit_begin,
+                                       const int32_t* unit_kend, float scale, int32_t n_splits,
+                                       void* out, void* stream);
+
+/*
  * ws_fm_euler_step -- one explicit Euler step of flow-matching latent
  * generation ([Summary] 核心方法 and Thinker-Performer架构: the performer
  * generates the next unit's latent by flow matching):
