@@ -62,6 +62,9 @@ def parse():
                    help="instead of the fixed unit step: --steps consecutive units on a growing "
                         "cache, each unit's slice appended on a second stream while the previous "
                         "unit denoises; also timed on one stream")
+    p.add_argument("--no-side", action="store_true",
+                   help="only the named workload's line: no side records of the other "
+                        "workloads and ops")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain copy (the append kernel) of known size, for "
                         "calibrating HBM byte counters")
@@ -127,7 +130,7 @@ class _Parity:
                 "within": self.max_abs <= PARITY_MAX_ABS and self.rel <= PARITY_REL_FRO}
 
 
-def cpu_baseline(w, budget_s: float, gpu_out=None):
+def cpu_baseline(w, budget_s: float, gpu_out=None, ops: bool = True):
     """Time the fp64 oracle on a bounded sample of the same workload: whole
     (denoise step, head) attention problems (all query rows over all keys),
     in step-then-head order, until about budget_s seconds of CPU time.
@@ -166,6 +169,14 @@ def cpu_baseline(w, budget_s: float, gpu_out=None):
         if elapsed >= budget_s:
             break
         hist = hist if len(hist) * w.cache_len * w.head_dim * 4 < (2 << 30) else {}
+    if not ops:
+        return {"value": round(flops / elapsed / 1e12, 5), "unit": "TFLOP/s",
+                "cores": int(threads), "kind": "oracle",
+                "sample": f"fp64 NumPy oracle on {done} of {w.steps * w.heads} (denoise step, "
+                          f"head) attention problems ({w.n_q} queries x {w.n_keys} keys each), "
+                          f"{elapsed:.2f} s of compute",
+                "attention_ms_per_problem": round(elapsed / done * 1e3, 2), "blas": blas,
+                **({"parity": parity.report()} if gpu_out is not None else {})}
     # the other two steps of the unit, once each: the slice append into a
     # cache of this length and one Euler step of the unit's latent
     ck = np.zeros((w.heads, w.cache_len + w.slice_tokens, w.head_dim), np.uint16)
@@ -187,11 +198,14 @@ def cpu_baseline(w, budget_s: float, gpu_out=None):
             **({"parity": parity.report()} if gpu_out is not None else {})}
 
 
-def roofline(w, attn_ms: list) -> dict:
+def roofline(w, attn_ms: list, step_ms: list | None = None) -> dict:
     """The attention kernel against the roofline that bounds it: the bf16
     MFMA peak above the ridge point (peak FLOP/s / peak B/s), HBM below it.
     Both fractions are given, from the average of the timed launches; their
-    minimum and 10th/50th/90th percentiles (nearest rank) are reported too."""
+    minimum and 10th/50th/90th percentiles (nearest rank) are reported too.
+    `frac`/`achieved` are the split-KV kernel's own launches (the dominant
+    kernel); step_ms (the split-KV launch plus its merge, the whole attention
+    of a denoise step), when given, is reported beside them as step_*."""
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     srt = sorted(attn_ms)
 
@@ -215,6 +229,12 @@ def roofline(w, attn_ms: list) -> dict:
          "launch_ms_avg": round(attn_avg_ms, 5), "launch_ms_min": round(srt[0], 5),
          "launch_ms_p10": round(pct(10), 5), "launch_ms_p50": round(pct(50), 5),
          "launch_ms_p90": round(pct(90), 5), "launches_timed": len(attn_ms)}
+    if step_ms:
+        st = sum(step_ms) / len(step_ms)
+        r.update({"step_ms_avg": round(st, 5),
+                  "step_frac": round((kv / (st * 1e-3) / 1e9 / PEAK_HBM_GBS) if hbm
+                                     else (flops / (st * 1e-3) / 1e12 / PEAK_BF16_TFLOPS), 4),
+                  "step_what": "split-KV launch + merge launch (events after the merge)"})
     return r
 
 
@@ -396,116 +416,166 @@ def calib_copy(steps: int) -> None:
                       "write_bytes_per_launch": nbytes, "launches": steps}))
 
 
-def op_bench(steps: int) -> None:
-    """HBM bandwidth of ws_kv_append on 952-token x 40-head token-major slices
-    (a v0.2 unit: 32 slice + 920 video tokens) and of ws_fm_euler_step on the
-    whole-performer latent (920 x 40 x 128). Sources and destinations rotate
-    over more than the 256 MB last-level cache, so the bytes come from HBM."""
+def _timed(calls: list, reps: int) -> float:
+    """GPU seconds per call: the calls are captured once into a HIP graph (the
+    library only enqueues kernels; torch's copy_ becomes a copy node) and the
+    graph is replayed reps times between two events. Back to back on the GPU
+    with no host work in between: a Python call costs more than these short
+    kernels take, so timing eager calls would measure the host."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for c in calls:                 # warm-up, outside the capture
+            c()
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * len(calls))
+
+
+def _bw(op: str, nbytes: int, per_s: float, **extra) -> dict:
+    gbs = nbytes / per_s / 1e9
+    return {"op": op, **extra, "us_per_call": round(per_s * 1e6, 3), "bytes_per_call": nbytes,
+            "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def op_records(steps: int) -> list:
+    """HBM bandwidth of the copy-like ops (GPU time per call from HIP-graph
+    replays of back-to-back calls), sources and destinations rotating over
+    more than the 256 MB last-level cache so that the bytes come from HBM:
+      * the unit-end append of the whole performer as one launch
+        (ws_kv_append_segments): 920 committed latent tokens, head-major, then
+        the next unit's 32-token slice, token-major, all 40 heads (952 rows);
+      * the same 952 rows from one token-major slice (ws_kv_append);
+      * the plain-copy ceiling for the same bytes measured in the same run:
+        one contiguous device-to-device copy of 2 x 952 x 40 x 128 bf16;
+      * ws_kv_append of a 16,384-token slice (670 MB moved);
+      * ws_fm_euler_step over the whole performer's latent (920 x 40 x 128)."""
     import torch
 
-    from cached_block_causal_amd import KVCache, fm_euler_step, kv_append
-    heads, d, n, nbuf = 40, 128, 952, 24
-    srcs = [(torch.randn(n, heads, d, device="cuda").to(torch.bfloat16),
-             torch.randn(n, heads, d, device="cuda").to(torch.bfloat16)) for _ in range(nbuf)]
+    from cached_block_causal_amd import (KVCache, fm_euler_step, kv_append,
+                                         kv_append_segments)
+    heads, d, nbuf = 40, 128, 24
+    n_commit, n_slice = 920, 32
+    n = n_commit + n_slice
+    recs = []
+    bf = torch.bfloat16
+    commits = [(torch.randn(heads, n_commit, d, device="cuda").to(bf),
+                torch.randn(heads, n_commit, d, device="cuda").to(bf)) for _ in range(nbuf)]
+    slices = [(torch.randn(n_slice, heads, d, device="cuda").to(bf),
+               torch.randn(n_slice, heads, d, device="cuda").to(bf)) for _ in range(nbuf)]
     cache = KVCache(heads, d, n * nbuf)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def appends():
-        cache.rewind(0)
-        for k, v in srcs:
-            kv_append(cache, k, v)
-
-    appends()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(steps):
-        appends()
-    ev1.record()
-    torch.cuda.synchronize()
-    per = ev0.elapsed_time(ev1) * 1e-3 / (steps * nbuf)
     nbytes = 2 * (2 * n * heads * d * 2)          # K and V, read + write
-    print(json.dumps({"op": "ws_kv_append", "tokens": n, "heads": heads, "head_dim": d,
-                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
-                      "GB_per_s": round(nbytes / per / 1e9, 1),
-                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
-    # the same kernel on a 16,384-token slice (670 MB moved per call)
+
+    def fused(i):
+        def call():
+            cache.rewind(i * n)
+            (ck, cv), (sk, sv) = commits[i], slices[i]
+            kv_append_segments(cache, [(ck, cv, "head", 0), (sk, sv, "token", 0)])
+        return call
+
+    per = _timed([fused(i) for i in range(nbuf)], steps)
+    recs.append(_bw("ws_kv_append_segments", nbytes, per, tokens=n, heads=heads, head_dim=d,
+                    what="unit end: 920 committed tokens (head-major) + 32-token slice "
+                         "(token-major) in one launch"))
+    tok = [(torch.randn(n, heads, d, device="cuda").to(bf),
+            torch.randn(n, heads, d, device="cuda").to(bf)) for _ in range(nbuf)]
+
+    def single(i):
+        def call():
+            cache.rewind(i * n)
+            kv_append(cache, tok[i][0], tok[i][1])
+        return call
+
+    per_single = _timed([single(i) for i in range(nbuf)], steps)
+    recs.append(_bw("ws_kv_append", nbytes, per_single, tokens=n, heads=heads, head_dim=d,
+                    what="one 952-token token-major slice"))
+    srcs = [torch.randn(2 * n * heads * d, device="cuda").to(bf) for _ in range(nbuf)]
+    dsts = [torch.empty_like(t) for t in srcs]
+
+    def plain(i):
+        return lambda: dsts[i].copy_(srcs[i])
+
+    per_copy = _timed([plain(i) for i in range(nbuf)], steps)
+    ceil = _bw("plain_copy", nbytes, per_copy, tokens=n, heads=heads, head_dim=d,
+               what="contiguous device-to-device copy of the same bytes (torch copy_)")
+    recs.append(ceil)
+    recs[0]["vs_plain_copy"] = round(per_copy / per, 4)
+    recs[1]["vs_plain_copy"] = round(per_copy / per_single, 4)
+    del commits, slices, tok, srcs, dsts, cache
     big_n = 16384
-    bk = torch.randn(big_n, heads, d, device="cuda").to(torch.bfloat16)
-    bv = torch.randn(big_n, heads, d, device="cuda").to(torch.bfloat16)
+    bk = torch.randn(big_n, heads, d, device="cuda").to(bf)
+    bv = torch.randn(big_n, heads, d, device="cuda").to(bf)
     big = KVCache(heads, d, big_n)
-    big.rewind(0)
-    kv_append(big, bk, bv)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(steps):
+
+    def large():
         big.rewind(0)
         kv_append(big, bk, bv)
-    ev1.record()
-    torch.cuda.synchronize()
-    per = ev0.elapsed_time(ev1) * 1e-3 / steps
-    nbytes = 2 * (2 * big_n * heads * d * 2)
-    print(json.dumps({"op": "ws_kv_append", "tokens": big_n, "heads": heads, "head_dim": d,
-                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
-                      "GB_per_s": round(nbytes / per / 1e9, 1),
-                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
+
+    recs.append(_bw("ws_kv_append", 2 * (2 * big_n * heads * d * 2), _timed([large], steps),
+                    tokens=big_n, heads=heads, head_dim=d))
     del bk, bv, big
     elems = 920 * 40 * 128
     xs = [torch.randn(elems, device="cuda") for _ in range(nbuf)]
-    vs = [torch.randn(elems, device="cuda").to(torch.bfloat16) for _ in range(nbuf)]
-    for x, v in zip(xs, vs):
-        fm_euler_step(x, v, 0.25)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(steps):
-        for x, v in zip(xs, vs):
-            fm_euler_step(x, v, 0.25)
-    ev1.record()
-    torch.cuda.synchronize()
-    per = ev0.elapsed_time(ev1) * 1e-3 / (steps * nbuf)
-    nbytes = elems * 10
-    print(json.dumps({"op": "ws_fm_euler_step", "elements": elems,
-                      "us_per_call": round(per * 1e6, 3), "bytes_per_call": nbytes,
-                      "GB_per_s": round(nbytes / per / 1e9, 1),
-                      "frac_hbm_peak": round(nbytes / per / 1e9 / PEAK_HBM_GBS, 4)}))
+    vs = [torch.randn(elems, device="cuda").to(bf) for _ in range(nbuf)]
+
+    def euler(i):
+        return lambda: fm_euler_step(xs[i], vs[i], 0.25)
+
+    recs.append(_bw("ws_fm_euler_step", elems * 10, _timed([euler(i) for i in range(nbuf)], steps),
+                    elements=elems))
+    return recs
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU Ulysses exchange is not built)", file=sys.stderr)
-        sys.exit(2)
+def op_bench(steps: int) -> None:
+    for r in op_records(steps):
+        print(json.dumps(r))
+
+
+def unit_bench(w, args, cpu_seconds: float, graph: bool = True, cpu_ops: bool = True) -> dict:
+    """One streaming unit of workload w, timed over args.steps units (after
+    args.warmup): one append launch for the unit's end (the previous unit's
+    committed latents, head-major, then this unit's slice, token-major, all
+    heads of the slice keeping this GPU's block), then per denoise step
+    ws_attn_partial + ws_attn_merge and ws_fm_euler_step. The cache is
+    rewound before every unit, so every unit is the same workload."""
+    import numpy as np
     import torch
 
-    import workloads as W
-    from cached_block_causal_amd import AttnCall, KVCache, fm_euler_step, kv_append
+    from cached_block_causal_amd import AttnCall, KVCache, fm_euler_step, kv_append_segments
+    from cached_block_causal_amd import kv_append
     from workloads import gen as G
     from workloads.device import dev_bits, host_bits
 
-    if args.calib_copy:
-        calib_copy(args.steps)
-        return
-    if args.op_bench:
-        op_bench(args.steps)
-        return
-    if args.pipeline:
-        pipeline_bench(W.BY_NAME[args.workload], args)
-        return
-
-    w = W.BY_NAME[args.workload]
-    if w.prefill:
-        prefill_bench(w, args)
-        return
     heads = list(range(w.head_begin, w.head_begin + w.heads))
     t_setup = time.perf_counter()
     cache = KVCache(w.heads, w.head_dim, w.capacity)
     for u in range(w.cached_units):                      # history (untimed)
         k, v = G.cache_unit_tokens(w, u, heads)
         kv_append(cache, dev_bits(k), dev_bits(v), layout="head")
-    history_len = cache.len
+    # the last history unit's tokens after its slice: re-committed each unit
+    ck, cv = G.cache_unit_tokens(w, w.cached_units - 1, heads)
+    commit_k = dev_bits(np.ascontiguousarray(ck[:, w.slice_tokens:]))
+    commit_v = dev_bits(np.ascontiguousarray(cv[:, w.slice_tokens:]))
+    rewind_to = cache.len - commit_k.shape[1]
     sk, sv = G.cache_unit_tokens(w, w.current_unit, range(w.heads_total), w.slice_tokens)
     slice_k, slice_v = dev_bits(G.token_major(sk)), dev_bits(G.token_major(sv))
-    kv_append(cache, slice_k, slice_v, head_begin=w.head_begin)
+    segments = [(commit_k, commit_v, "head", 0), (slice_k, slice_v, "token", w.head_begin)]
+    cache.rewind(rewind_to)
+    kv_append_segments(cache, segments)
+    assert cache.len == w.cache_len
     steps_in = [G.step_tensors(w, s) for s in range(w.steps)]
     dq = [dev_bits(t[0]) for t in steps_in]
     dks = [dev_bits(t[1]) for t in steps_in]
@@ -533,12 +603,11 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     n_attn = args.steps * w.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_attn)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_attn)]
 
     def unit_step(timed_events=None, per_step=None):
-        cache.rewind(history_len)
-        kv_append(cache, slice_k, slice_v, head_begin=w.head_begin)
+        cache.rewind(rewind_to)
+        kv_append_segments(cache, segments)    # previous unit's commit + this unit's slice
         for s in range(w.steps):
             step_calls = [calls[s]] if per_step is None else per_step[s]
             if timed_events is not None:
@@ -549,8 +618,9 @@ def main():
                 timed_events[s][1].record()
             for c in step_calls:
                 c.merge()
+            if timed_events is not None:
+                timed_events[s][2].record()
             fm_euler_step(x, dvel[s], w.dt)
-        kv_append(cache, dks[-1], dvs[-1], layout="head")   # commit the unit's latents
 
     for _ in range(args.warmup):
         unit_step()
@@ -565,8 +635,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
-    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    attn_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
 
     flops_step = w.attn_flops()
     value = flops_step * w.steps / (ms_per_step * 1e-3) / 1e12
@@ -587,8 +657,10 @@ def main():
         "config": {"workload": w.name, "heads": w.heads, "heads_total": w.heads_total,
                    "head_dim": w.head_dim, "n_q": w.n_q, "cache_len": w.cache_len,
                    "n_keys": w.n_keys, "denoise_steps": w.steps, "splits": splits,
-                   "slice_tokens": w.slice_tokens, "commit_tokens": w.n_self},
-        "roofline": roofline(w, attn_ms),
+                   "append_tokens": w.unit_tokens,
+                   "append": "one launch: %d committed + %d slice tokens"
+                             % (commit_k.shape[1], w.slice_tokens)},
+        "roofline": roofline(w, attn_ms, step_ms),
         "us_per_unit": round(ms_per_step * 1e3, 1),
         "unit_budget_frac": round(ms_per_step / UNIT_BUDGET_MS, 5),
         "attention_layers_per_unit_budget": int(UNIT_BUDGET_MS // ms_per_step),
@@ -606,15 +678,79 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         sep_ms = t0.elapsed_time(t1) / args.steps
-        sep_attn = [a.elapsed_time(b) for a, b in ev]
+        sep_attn = [a.elapsed_time(b) for a, b, _ in ev]
         out["separate"] = {"ms_per_step": round(sep_ms, 4),
                            "attention_ms_avg": round(sum(sep_attn) / len(sep_attn), 5),
                            "splits": [c.splits for c in sep_calls[0]],
                            "what": "one call for the audio and one for the video queries per "
                                    "denoise step, attention time = both partial launches"}
-    out["graph"] = graph_replay(unit_step, args.steps)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, [host_bits(c.out) for c in calls])
+    if graph:
+        out["graph"] = graph_replay(unit_step, args.steps)
+    if cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, cpu_seconds, [host_bits(c.out) for c in calls],
+                                           ops=cpu_ops)
+    return out
+
+
+# workloads whose records ride along in the default bench line, and the
+# oracle time each gets (seconds) for its bounded parity sample
+SIDE_WORKLOADS = (("v02_whole_performer", 4.0), ("audio_long_history", 4.0), ("v01_unit", 3.0))
+
+
+def side_record(rec: dict) -> dict:
+    """The parts of a workload's unit record that the default line carries."""
+    keep = ("value", "unit", "ms_per_step", "us_per_unit", "unit_budget_frac",
+            "attention_layers_per_unit_budget", "setup_s")
+    out = {k: rec[k] for k in keep if k in rec}
+    out["config"] = {k: rec["config"][k] for k in ("heads", "head_dim", "n_q", "n_keys", "splits")}
+    r = rec["roofline"]
+    out["roofline"] = {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
+                                         "mfma_frac", "hbm_frac", "launch_ms_avg", "launch_ms_p50",
+                                         "step_ms_avg", "step_frac") if k in r}
+    if "cpu_baseline" in rec:
+        c = rec["cpu_baseline"]
+        out["cpu_baseline"] = {k: c[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                 "parity") if k in c}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU Ulysses exchange is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+
+    if args.calib_copy:
+        calib_copy(args.steps)
+        return
+    if args.op_bench:
+        op_bench(args.steps)
+        return
+    if args.pipeline:
+        pipeline_bench(W.BY_NAME[args.workload], args)
+        return
+
+    w = W.BY_NAME[args.workload]
+    if w.prefill:
+        prefill_bench(w, args)
+        return
+    out = unit_bench(w, args, 0.0 if args.no_cpu_baseline else args.cpu_seconds)
+    if not args.no_side and args.workload == "v02_rank_share" and args.splits == 0:
+        # the other targets, in the same run and line: each workload's unit
+        # (fewer timed units) with a bounded oracle parity sample, and the ops
+        side = argparse.Namespace(**vars(args))
+        side.steps, side.warmup = min(args.steps, 10), min(args.warmup, 2)
+        out["workloads"] = {}
+        for name, secs in SIDE_WORKLOADS:
+            rec = unit_bench(W.BY_NAME[name], side, 0.0 if args.no_cpu_baseline else secs,
+                             graph=False, cpu_ops=False)
+            out["workloads"][name] = side_record(rec)
+            torch.cuda.empty_cache()
+        out["ops"] = op_records(min(args.steps, 10))
     print(json.dumps(out), flush=True)
 
 

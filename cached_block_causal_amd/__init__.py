@@ -5,7 +5,7 @@ of include/ws.h). This package holds the kernel sources (csrc/), the build
 script and a thin PyTorch binding; importing the binding needs the built
 library and raises if it is missing.
 """
-__all__ = ["KVCache", "kv_append", "block_causal_attn", "block_causal_attn_noalloc", "AttnCall",
+__all__ = ["KVCache", "kv_append", "kv_append_segments", "block_causal_attn", "block_causal_attn_noalloc", "AttnCall",
            "attn_default_splits",
            "attn_workspace_bytes", "fm_euler_step", "UnitInputs", "run_units"]
 

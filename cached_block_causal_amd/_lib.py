@@ -33,6 +33,18 @@ class WsKvCache(ctypes.Structure):
     ]
 
 
+class WsKvSegment(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("n_tok", ctypes.c_int32),
+        ("src_heads", ctypes.c_int32),
+        ("head_begin", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+    ]
+
+
+WS_MAX_SEGMENTS = 4
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
 # name -> (restype, argtypes), exactly as declared in include/ws.h
@@ -40,6 +52,8 @@ SIGNATURES = {
     "ws_kv_append": (ctypes.c_int, [ctypes.POINTER(WsKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_void_p]),
+    "ws_kv_append_segments": (ctypes.c_int, [ctypes.POINTER(WsKvCache), ctypes.POINTER(WsKvSegment),
+                                             ctypes.c_int32, ctypes.c_void_p]),
     "ws_attn_default_splits": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int64]),
     "ws_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -290,37 +290,69 @@ ws_status plan_attn(const ws_kv_cache* cache, const void* q, int32_t n_q, const 
 
 extern "C" {
 
-ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src, int32_t n_tok,
-                       int32_t src_heads, int32_t head_begin, int32_t layout, void* stream) {
+ws_status ws_kv_append_segments(ws_kv_cache* cache, const ws_kv_segment* segs, int32_t n_segs,
+                                 void* stream) {
   g_last_error.clear();
   ws_status st = check_cache(cache);
   if (st != WS_OK) return st;
-  if (layout != WS_TOKEN_MAJOR && layout != WS_HEAD_MAJOR)
-    return fail(WS_ERR_UNSUPPORTED, "unknown source layout %d", layout);
-  if (n_tok < 0) return fail(WS_ERR_SHAPE, "n_tok %d < 0", n_tok);
-  if (src_heads < 1 || head_begin < 0 || (int64_t)head_begin + cache->heads > src_heads)
-    return fail(WS_ERR_SHAPE, "head block [%d, %lld) outside the %d source heads", head_begin,
-                (long long)head_begin + cache->heads, src_heads);
-  if ((int64_t)cache->len + n_tok > cache->capacity)
-    return fail(WS_ERR_CAPACITY, "len %d + n_tok %d > capacity %d", cache->len, n_tok,
-                cache->capacity);
-  if (n_tok == 0) return WS_OK;
-  if ((int64_t)n_tok * (cache->head_dim / 8) > 0x7FFFFFFF || cache->heads > 65535)
-    return fail(WS_ERR_SHAPE, "append of %d tokens x %d heads is too large for one launch", n_tok,
-                cache->heads);
-  if (!cache->k || !cache->v || !k_src || !v_src) return fail(WS_ERR_NULL, "a buffer is NULL");
-  if (!aligned16(cache->k) || !aligned16(cache->v) || !aligned16(k_src) || !aligned16(v_src))
-    return fail(WS_ERR_ALIGN, "a device pointer is not 16-byte aligned");
-  st = hip_status(ws::launch_kv_append(static_cast<uint16_t*>(cache->k),
-                                       static_cast<uint16_t*>(cache->v),
-                                       static_cast<const uint16_t*>(k_src),
-                                       static_cast<const uint16_t*>(v_src), cache->heads,
-                                       cache->head_dim, cache->capacity, cache->len, n_tok,
-                                       src_heads, head_begin, layout,
-                                       static_cast<hipStream_t>(stream)),
+  if (!segs) return fail(WS_ERR_NULL, "segment table is NULL");
+  if (n_segs < 1 || n_segs > WS_MAX_SEGMENTS)
+    return fail(WS_ERR_SHAPE, "n_segs %d outside [1, %d]", n_segs, WS_MAX_SEGMENTS);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const ws_kv_segment& g = segs[i];
+    if (g.layout != WS_TOKEN_MAJOR && g.layout != WS_HEAD_MAJOR)
+      return fail(WS_ERR_UNSUPPORTED, "segment %d: unknown source layout %d", i, g.layout);
+    if (g.n_tok < 0) return fail(WS_ERR_SHAPE, "segment %d: n_tok %d < 0", i, g.n_tok);
+    if (g.src_heads < 1 || g.head_begin < 0 || (int64_t)g.head_begin + cache->heads > g.src_heads)
+      return fail(WS_ERR_SHAPE, "segment %d: head block [%d, %lld) outside the %d source heads", i,
+                  g.head_begin, (long long)g.head_begin + cache->heads, g.src_heads);
+    total += g.n_tok;
+  }
+  if ((int64_t)cache->len + total > cache->capacity)
+    return fail(WS_ERR_CAPACITY, "len %d + %lld tokens > capacity %d", cache->len,
+                (long long)total, cache->capacity);
+  if (total == 0) return WS_OK;
+  if (total * (cache->head_dim / 8) > 0x7FFFFFFF || cache->heads > 65535)
+    return fail(WS_ERR_SHAPE, "append of %lld tokens x %d heads is too large for one launch",
+                (long long)total, cache->heads);
+  if (!cache->k || !cache->v) return fail(WS_ERR_NULL, "a cache buffer is NULL");
+  if (!aligned16(cache->k) || !aligned16(cache->v))
+    return fail(WS_ERR_ALIGN, "a cache buffer is not 16-byte aligned");
+  ws::AppendArgs a;
+  memset(&a, 0, sizeof a);
+  for (int32_t i = 0; i < n_segs; ++i) {
+    const ws_kv_segment& g = segs[i];
+    if (g.n_tok == 0) continue;
+    if (!g.k || !g.v) return fail(WS_ERR_NULL, "segment %d: a buffer is NULL", i);
+    if (!aligned16(g.k) || !aligned16(g.v))
+      return fail(WS_ERR_ALIGN, "segment %d: a buffer is not 16-byte aligned", i);
+    ws::AppendSeg& s = a.seg[a.n_segs++];
+    s.k = static_cast<const uint16_t*>(g.k);
+    s.v = static_cast<const uint16_t*>(g.v);
+    s.n_tok = g.n_tok;
+    s.src_heads = g.src_heads;
+    s.head_begin = g.head_begin;
+    s.layout = g.layout;
+    s.row0 = a.total_tok;
+    a.total_tok += g.n_tok;
+  }
+  a.ck = static_cast<uint16_t*>(cache->k);
+  a.cv = static_cast<uint16_t*>(cache->v);
+  a.cache_head_stride = (int64_t)cache->capacity * cache->head_dim;
+  a.len = cache->len;
+  a.head_dim = cache->head_dim;
+  a.log2_cpr = cache->head_dim == 128 ? 4 : 3;
+  st = hip_status(ws::launch_kv_append(a, cache->heads, static_cast<hipStream_t>(stream)),
                   "kv_append launch");
-  if (st == WS_OK) cache->len += n_tok;
+  if (st == WS_OK) cache->len += (int32_t)total;
   return st;
+}
+
+ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src, int32_t n_tok,
+                       int32_t src_heads, int32_t head_begin, int32_t layout, void* stream) {
+  const ws_kv_segment g = {k_src, v_src, n_tok, src_heads, head_begin, layout};
+  return ws_kv_append_segments(cache, &g, 1, stream);
 }
 
 int32_t ws_attn_default_splits(int32_t heads, int32_t n_q, int32_t head_dim, int64_t n_keys) {

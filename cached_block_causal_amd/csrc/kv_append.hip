@@ -5,8 +5,11 @@
 // its own pre-split cache positions; nothing else moves.)
 //
 // Pure data movement, bound by HBM: 2 * n * heads * D * 2 bytes read and the
-// same written per call (K and V). One workgroup covers 256 x 4 consecutive
-// 16-byte chunks of one head (the D/8 chunks of a row fastest, then tokens):
+// same written per call (K and V). A call may gather up to four source
+// segments (e.g. a unit's committed latents, head-major, then the next
+// slice, token-major) into consecutive rows with one launch. One workgroup
+// covers 256 x 4 consecutive 16-byte chunks of one head (the D/8 chunks of a
+// row fastest, then tokens):
 // each thread issues its four loads before its four stores, consecutive lanes
 // write consecutive cache addresses and read whole 128/256-byte rows of the
 // source, and the (token, chunk) split is a shift and a mask. Loads and stores
@@ -20,48 +23,52 @@ namespace ws {
 
 constexpr int kAppendUnroll = 4;  // 16-byte chunks in flight per thread
 
-// grid: x over the (token, chunk) pairs of one head, y = head, z = K (0) / V (1)
-__global__ __launch_bounds__(256) void kv_append_kernel(
-    uint16_t* __restrict__ ck, uint16_t* __restrict__ cv,
-    const uint16_t* __restrict__ sk, const uint16_t* __restrict__ sv,
-    int head_dim, int log2_cpr, int64_t cache_head_stride, int len, int n_tok, int src_heads,
-    int head_begin, int layout) {
-  uint16_t* __restrict__ dst = blockIdx.z == 0 ? ck : cv;
-  const uint16_t* __restrict__ src = blockIdx.z == 0 ? sk : sv;
+// grid: x over the blocks of all segments (segment s owns blocks
+// [seg[s].blk0, seg[s + 1].blk0), each 256 x 4 chunks of its tokens), y =
+// head, z = K (0) / V (1). The segment is uniform per workgroup, so the
+// per-chunk addressing is a shift, a mask and one multiply-add.
+__global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
+  const int b = blockIdx.x;
+  AppendSeg g = a.seg[0];
+#pragma unroll
+  for (int q = 1; q < kAppendMaxSegs; ++q)
+    if (q < a.n_segs && b >= a.seg[q].blk0) g = a.seg[q];
+  uint16_t* __restrict__ dst = blockIdx.z == 0 ? a.ck : a.cv;
+  const uint16_t* __restrict__ src = blockIdx.z == 0 ? g.k : g.v;
   const int h = blockIdx.y;
-  const int per_head = n_tok << log2_cpr;  // 16-byte chunks of this head's rows
-  const int cmask = (1 << log2_cpr) - 1;
-  const int base = blockIdx.x * (256 * kAppendUnroll) + threadIdx.x;
-  const int64_t src_h = layout == WS_TOKEN_MAJOR ? (int64_t)(head_begin + h) * head_dim
-                                                 : (int64_t)(head_begin + h) * n_tok * head_dim;
-  const int64_t src_t = layout == WS_TOKEN_MAJOR ? (int64_t)src_heads * head_dim : head_dim;
-  uint16_t* const dst_h = dst + h * cache_head_stride + (int64_t)len * head_dim;
+  const int per_seg = g.n_tok << a.log2_cpr;  // 16-byte chunks of this head's rows
+  const int cmask = (1 << a.log2_cpr) - 1;
+  const int base = (b - g.blk0) * (256 * kAppendUnroll) + threadIdx.x;
+  const int64_t src_h = g.layout == WS_TOKEN_MAJOR ? (int64_t)(g.head_begin + h) * a.head_dim
+                                                   : (int64_t)(g.head_begin + h) * g.n_tok * a.head_dim;
+  const int64_t src_t = g.layout == WS_TOKEN_MAJOR ? (int64_t)g.src_heads * a.head_dim : a.head_dim;
+  uint16_t* const dst_h = dst + h * a.cache_head_stride + (int64_t)(a.len + g.row0) * a.head_dim;
   u32x4 v[kAppendUnroll];
 #pragma unroll
   for (int j = 0; j < kAppendUnroll; ++j) {  // all loads first, then the stores
     const int i = base + j * 256;
-    if (i < per_head)
+    if (i < per_seg)
       v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          src + src_h + (int64_t)(i >> log2_cpr) * src_t + (i & cmask) * 8));
+          src + src_h + (int64_t)(i >> a.log2_cpr) * src_t + (i & cmask) * 8));
   }
 #pragma unroll
   for (int j = 0; j < kAppendUnroll; ++j) {
     const int i = base + j * 256;
-    if (i < per_head)
+    if (i < per_seg)
       __builtin_nontemporal_store(
-          v[j], reinterpret_cast<u32x4*>(dst_h + (int64_t)(i >> log2_cpr) * head_dim + (i & cmask) * 8));
+          v[j], reinterpret_cast<u32x4*>(dst_h + (int64_t)(i >> a.log2_cpr) * a.head_dim + (i & cmask) * 8));
   }
 }
 
-hipError_t launch_kv_append(uint16_t* ck, uint16_t* cv, const uint16_t* sk, const uint16_t* sv,
-                            int heads, int head_dim, int capacity, int len, int n_tok,
-                            int src_heads, int head_begin, int layout, hipStream_t stream) {
-  const int log2_cpr = head_dim == 128 ? 4 : 3;
-  const int64_t per_head = (int64_t)n_tok << log2_cpr;
-  const unsigned bx = (unsigned)((per_head + 256 * kAppendUnroll - 1) / (256 * kAppendUnroll));
-  hipLaunchKernelGGL(kv_append_kernel, dim3(bx, heads, 2), dim3(256), 0, stream, ck, cv, sk, sv,
-                     head_dim, log2_cpr, (int64_t)capacity * head_dim, len, n_tok, src_heads,
-                     head_begin, layout);
+hipError_t launch_kv_append(const AppendArgs& args, int heads, hipStream_t stream) {
+  AppendArgs a = args;
+  int blocks = 0;
+  for (int s = 0; s < a.n_segs; ++s) {
+    a.seg[s].blk0 = blocks;
+    const int64_t chunks = (int64_t)a.seg[s].n_tok << a.log2_cpr;
+    blocks += (int)((chunks + 256 * kAppendUnroll - 1) / (256 * kAppendUnroll));
+  }
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks, heads, 2), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

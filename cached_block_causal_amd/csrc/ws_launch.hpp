@@ -9,10 +9,24 @@
 
 namespace ws {
 
-// Cache append (bit copy of one head block of a slice into cache rows).
-hipError_t launch_kv_append(uint16_t* ck, uint16_t* cv, const uint16_t* sk, const uint16_t* sv,
-                            int heads, int head_dim, int capacity, int len, int n_tok,
-                            int src_heads, int head_begin, int layout, hipStream_t stream);
+// Cache append: bit copies of one head block of up to kAppendMaxSegs source
+// segments into consecutive cache rows [len, len + total_tok).
+constexpr int kAppendMaxSegs = WS_MAX_SEGMENTS;
+struct AppendSeg {
+  const uint16_t* k;
+  const uint16_t* v;
+  int n_tok, src_heads, head_begin, layout;
+  int row0;                 // first token of this segment within the call
+  int blk0;                 // first block of this segment (set by the launcher)
+};
+struct AppendArgs {
+  uint16_t* ck;
+  uint16_t* cv;
+  int64_t cache_head_stride;  // capacity * D (elements)
+  int len, head_dim, log2_cpr, total_tok, n_segs;
+  AppendSeg seg[kAppendMaxSegs];
+};
+hipError_t launch_kv_append(const AppendArgs& a, int heads, hipStream_t stream);
 
 // Euler update x = fma(dt, v, x).
 hipError_t launch_fm_euler(float* x, const uint16_t* v, int64_t n, float dt, hipStream_t stream);

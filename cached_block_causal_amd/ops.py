@@ -87,6 +87,31 @@ def kv_append(cache: KVCache, k_src: torch.Tensor, v_src: torch.Tensor, head_beg
     L.check(st, "ws_kv_append")
 
 
+def kv_append_segments(cache: KVCache, segments) -> None:
+    """ws_kv_append_segments: segments = [(k_src, v_src, layout, head_begin)],
+    layout 'token' ([n][H][D]) or 'head' ([H][n][D]); written to consecutive
+    rows in one launch."""
+    segs = (L.WsKvSegment * max(1, len(segments)))()
+    stream = None
+    for i, (k_src, v_src, layout, head_begin) in enumerate(segments):
+        if layout not in ("token", "head"):
+            raise ValueError("layout must be 'token' or 'head'")
+        if k_src.dim() != 3 or k_src.shape != v_src.shape:
+            raise ValueError("k_src/v_src must be equal 3-d tensors")
+        n, h = ((k_src.shape[0], k_src.shape[1]) if layout == "token"
+                else (k_src.shape[1], k_src.shape[0]))
+        segs[i] = L.WsKvSegment(_dev16(k_src, "k_src").value, _dev16(v_src, "v_src").value, n, h,
+                                head_begin, L.WS_TOKEN_MAJOR if layout == "token" else L.WS_HEAD_MAJOR)
+        stream = _stream(k_src)
+    st = L.lib().ws_kv_append_segments(ctypes.byref(cache.struct), segs, len(segments),
+                                       stream if stream is not None else _stream_default())
+    L.check(st, "ws_kv_append_segments")
+
+
+def _stream_default() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
 def attn_default_splits(heads: int, n_q: int, head_dim: int, n_keys: int) -> int:
     return int(L.lib().ws_attn_default_splits(heads, n_q, head_dim, n_keys))
 

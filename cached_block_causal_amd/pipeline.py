@@ -1,20 +1,23 @@
-"""Consecutive streaming units on one GPU's growing cache, with each unit's
-thinker-slice append overlapped with the previous unit's denoising.
+"""Consecutive streaming units on one GPU's growing cache, each unit's end
+(its committed latents and the next unit's thinker slice) written with one
+append launch that runs beside the unit's last denoise step.
 
 The pages' schedule overlaps adjacent units, and each unit's committed
 latents condition the later ones ("Wan-Streamer v0.2：更高分辨率，相同延迟",
 方法步骤详情; "Technical Summary: Wan-Streamer v0.2", Methodology, "The
 Performer"). Unit k on this GPU:
-  1. its slice is appended to the cache (this GPU's head block);
-  2. each denoise step runs attention over the cache plus the unit's own
+  1. each denoise step runs attention over the cache plus the unit's own
      tokens (partial + merge) and the Euler update of the unit's latent;
-  3. the unit's latent K/V are committed to the cache.
-With `overlap`, every slice append runs on a second stream. Unit k+1's slice
-is enqueued right after unit k's commit is enqueued, so the host assigns it
-the rows behind the commit, and it runs while unit k still denoises: unit
-k's attention reads only rows below its own end and the commit writes the
-rows before the slice, so the two streams never touch the same rows. Unit
-k+1's first attention waits for its slice with an event.
+  2. at its end, the unit's latent K/V (the last step's own tokens) and unit
+     k+1's slice are appended, in that order, with one launch
+     (ws_kv_append_segments). Unit 0's slice is appended first on its own.
+With `overlap`, the appends run on a second stream: the unit-end append is
+enqueued right after the last step's attention pass, so it runs beside that
+pass, its merge and the Euler update. The host enqueues that pass first, so
+the pass covers exactly the rows up to the unit's slice, and the append
+writes the rows behind them, which no pass of unit k reads. Unit k+1's first
+attention waits for the append with an event. Without `overlap`, everything
+runs in that order on one stream.
 
 Host orchestration only (streams, events, argument order); every step runs
 in the library's kernels through the binding.
@@ -45,8 +48,8 @@ def run_units(cache: ops.KVCache, units: list, dt: float, overlap: bool = True,
               side_stream: torch.cuda.Stream | None = None, n_splits: int = 0,
               attn_events: list | None = None) -> None:
     """Enqueue `units` back to back on the current stream (and `side_stream`
-    for the slice appends when `overlap`). Nothing is synchronised; the
-    cache length advances on the host as the calls are enqueued.
+    for the appends when `overlap`). Nothing is synchronised; the cache
+    length advances on the host as the calls are enqueued.
     attn_events[i][s] (optional) is a pair of timing events recorded around
     unit i's step-s attention launch."""
     main = torch.cuda.current_stream()
@@ -55,21 +58,30 @@ def run_units(cache: ops.KVCache, units: list, dt: float, overlap: bool = True,
         side = side_stream if side_stream is not None else torch.cuda.Stream()
         side.wait_stream(main)     # earlier work on the cache comes first
 
-    def append_slice(u: UnitInputs):
+    def append(segments):
         if side is None:
-            ops.kv_append(cache, u.slice_k, u.slice_v, head_begin=u.head_begin)
+            ops.kv_append_segments(cache, segments)
             return None
         with torch.cuda.stream(side):
-            ops.kv_append(cache, u.slice_k, u.slice_v, head_begin=u.head_begin)
+            ops.kv_append_segments(cache, segments)
         ev = torch.cuda.Event()
         ev.record(side)
         return ev
 
-    ready = append_slice(units[0]) if units else None
+    ready = None
+    if units:
+        u0 = units[0]
+        ready = append([(u0.slice_k, u0.slice_v, "token", u0.head_begin)])
     for i, u in enumerate(units):
         if ready is not None:
             main.wait_event(ready)
         ws = None
+        # unit end: this unit's latents, then the next unit's slice
+        end = [(u.commit_k, u.commit_v, "head", 0)]
+        if i + 1 < len(units):
+            n = units[i + 1]
+            end.append((n.slice_k, n.slice_v, "token", n.head_begin))
+        last = len(u.steps) - 1
         for s, (q, ks, vs, vel) in enumerate(u.steps):
             out = u.outs[s] if u.outs else None
             call = ops.AttnCall(cache, q, ks, vs, n_splits=n_splits, out=out, workspace=ws)
@@ -79,8 +91,9 @@ def run_units(cache: ops.KVCache, units: list, dt: float, overlap: bool = True,
             call.partial()
             if attn_events is not None:
                 attn_events[i][s][1].record()
+            if s == last and side is not None:
+                ready = append(end)          # beside this pass, merge and Euler
             call.merge()
             ops.fm_euler_step(u.x, vel, dt)
-        ops.kv_append(cache, u.commit_k, u.commit_v, layout="head")
-        if i + 1 < len(units):
-            ready = append_slice(units[i + 1])
+        if side is None:
+            append(end)

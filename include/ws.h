@@ -106,6 +106,33 @@ ws_status ws_kv_append(ws_kv_cache* cache, const void* k_src, const void* v_src,
                        int32_t layout, void* stream);
 
 /*
+ * ws_kv_append_segments -- ws_kv_append of up to WS_MAX_SEGMENTS sources into
+ * consecutive cache rows with one launch: segment i's tokens land right after
+ * segment i-1's. A unit's end is two such writes ([Summary] 方法步骤详情: the
+ * performer keeps what it generated as history, and the thinker's next slice
+ * follows it): the unit's committed latents (head-major, already on this GPU)
+ * and the next unit's slice (token-major); as one launch they are one
+ * 952-token write at the v0.2 sizes instead of a 920- and a 32-token one.
+ *   Each segment follows ws_kv_append's rules (layout, n_tok >= 0, head
+ *   block inside its src_heads); segments with n_tok == 0 are skipped and may
+ *   have NULL buffers. len + sum(n_tok) <= capacity.
+ * Errors as ws_kv_append, plus WS_ERR_NULL (segs NULL) and WS_ERR_SHAPE
+ * (n_segs outside [1, WS_MAX_SEGMENTS]). All or nothing: on error nothing is
+ * written and len is unchanged.
+ */
+#define WS_MAX_SEGMENTS 4
+typedef struct ws_kv_segment {
+  const void* k;        /* device bf16 source in `layout`                   */
+  const void* v;
+  int32_t n_tok;        /* tokens of this segment (>= 0)                    */
+  int32_t src_heads;    /* heads in the source                              */
+  int32_t head_begin;   /* first source head of this cache's block          */
+  int32_t layout;       /* WS_TOKEN_MAJOR or WS_HEAD_MAJOR                  */
+} ws_kv_segment;
+ws_status ws_kv_append_segments(ws_kv_cache* cache, const ws_kv_segment* segs,
+                                int32_t n_segs, void* stream);
+
+/*
  * Split-KV planning. The key range of each query tile is cut into n_splits
  * contiguous chunks processed by separate workgroups and merged by
  * log-sum-exp weights. ws_attn_default_splits returns the library's choice

@@ -22,7 +22,7 @@ def test_help_lists_the_modes():
     r = _run("--help")
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--workload", "--pipeline", "--op-bench",
-                 "--calib-copy", "--no-cpu-baseline"):
+                 "--calib-copy", "--no-cpu-baseline", "--no-side"):
         assert flag in r.stdout
 
 
@@ -42,6 +42,8 @@ def test_roofline_block_fields_and_percentiles():
     assert (r["launch_ms_min"], r["launch_ms_p10"], r["launch_ms_p50"], r["launch_ms_p90"]) == \
         (0.28, 0.28, 0.305, 0.33)
     assert r["launches_timed"] == 10
+    s = bench.roofline(W.BY_NAME["v02_rank_share"], times, [t + 0.01 for t in times])
+    assert abs(s["step_ms_avg"] - (avg + 0.01)) < 1e-9 and s["step_frac"] < s["frac"]
     a = bench.roofline(W.BY_NAME["audio_long_history"], [0.8])
     assert a["bound"] == "hbm" and a["unit"] == "GB/s" and a["kernel"].startswith("attn_narrow")
     assert abs(a["achieved"] - W.BY_NAME["audio_long_history"].attn_kv_bytes() / 0.8e-3 / 1e9) < 0.1

@@ -73,6 +73,30 @@ def test_append_validation(lib):
     assert c.len == 10
 
 
+def test_append_segments_validation(lib):
+    c = _cache()
+    def segs(*items):
+        arr = (L.WsKvSegment * max(1, len(items)))()
+        for i, it in enumerate(items):
+            arr[i] = L.WsKvSegment(*it)
+        return arr
+    ok = (FAKE, FAKE, 5, 4, 0, L.WS_TOKEN_MAJOR)
+    empty = (None, None, 0, 4, 0, L.WS_HEAD_MAJOR)
+    call = lambda s, n: lib.ws_kv_append_segments(ctypes.byref(c), s, n, None)
+    assert lib.ws_kv_append_segments(ctypes.byref(c), None, 1, None) == L.WS_ERR_NULL
+    assert call(segs(ok), 0) == L.WS_ERR_SHAPE
+    assert call(segs(ok, ok, ok, ok, ok), 5) == L.WS_ERR_SHAPE
+    assert call(segs(ok, (FAKE, FAKE, 5, 4, 0, 2)), 2) == L.WS_ERR_UNSUPPORTED
+    assert call(segs(ok, (FAKE, FAKE, -1, 4, 0, 0)), 2) == L.WS_ERR_SHAPE
+    assert call(segs(ok, (FAKE, FAKE, 5, 4, 3, 0)), 2) == L.WS_ERR_SHAPE   # heads [3, 5) of 4
+    # 45 + 46 tokens do not fit the 90 free rows: refused as a whole
+    assert call(segs((FAKE, FAKE, 45, 4, 0, 0), (FAKE, FAKE, 46, 2, 0, 1)), 2) == L.WS_ERR_CAPACITY
+    assert c.len == 10 and "capacity" in _err(lib)
+    assert call(segs(ok, (None, FAKE, 5, 4, 0, 0)), 2) == L.WS_ERR_NULL
+    assert call(segs((FAKE + 8, FAKE, 5, 4, 0, 0), ok), 2) == L.WS_ERR_ALIGN
+    assert call(segs(empty, empty), 2) == L.WS_OK and c.len == 10     # nothing to write
+
+
 def _attn(lib, cache, **kw):
     a = dict(q=FAKE, nq=50, ks=None, vs=None, ns=0, units=1, qb=[0, 50], kend=[10], scale=0.1,
              splits=1, out=FAKE, ws=None, wsb=0)

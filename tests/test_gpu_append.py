@@ -94,3 +94,71 @@ def test_empty_append_is_noop():
     src = dev_bits(np.zeros((0, 2, 128), dtype=np.uint16))
     kv_append(cache, src, src)
     assert cache.len == 0
+
+
+@pytest.mark.parametrize("w", W.STREAMING, ids=[w.name for w in W.STREAMING])
+def test_unit_end_fused_append_bit_exact(w):
+    """A unit's end as one launch (ws_kv_append_segments): its committed
+    latents (head-major, this GPU's heads) then the next unit's slice
+    (token-major, all heads of the slice, keeping this GPU's block), written
+    behind existing rows; equal bit for bit to the oracle's two appends in
+    that order, everything else untouched."""
+    need_gpu()
+    from cached_block_causal_amd import kv_append, kv_append_segments
+    print(f"fused append {w.name}", flush=True)
+    d, hr = w.head_dim, w.heads
+    own = range(w.head_begin, w.head_begin + hr)
+    n_commit = w.unit_tokens - w.slice_tokens
+    start = 29
+    cap = start + n_commit + w.slice_tokens + 9
+    cache = poisoned_cache(hr, d, cap)
+    pre_k, pre_v = G.cache_unit_tokens(w, 998, own, start)
+    kv_append(cache, dev_bits(pre_k), dev_bits(pre_v), layout="head")
+    ck, cv = G.cache_unit_tokens(w, 6, own, w.unit_tokens)
+    ck, cv = np.ascontiguousarray(ck[:, w.slice_tokens:]), np.ascontiguousarray(cv[:, w.slice_tokens:])
+    sk, sv = G.cache_unit_tokens(w, 7, range(w.heads_total), w.slice_tokens)
+    sk, sv = G.token_major(sk), G.token_major(sv)
+    kv_append_segments(cache, [(dev_bits(ck), dev_bits(cv), "head", 0),
+                               (dev_bits(sk), dev_bits(sv), "token", w.head_begin)])
+    torch.cuda.synchronize()
+    assert cache.len == start + n_commit + w.slice_tokens
+    ek, ev, el = O.kv_append(_poison_np(hr, cap, d), _poison_np(hr, cap, d), 0, pre_k, pre_v, 0,
+                             O.HEAD_MAJOR)
+    ek, ev, el = O.kv_append(ek, ev, el, ck, cv, 0, O.HEAD_MAJOR)
+    ek, ev, el = O.kv_append(ek, ev, el, sk, sv, w.head_begin, O.TOKEN_MAJOR)
+    assert el == cache.len
+    assert np.array_equal(host_bits(cache.k), ek)
+    assert np.array_equal(host_bits(cache.v), ev)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_four_segments_with_an_empty_one(head_dim):
+    """Four segments of mixed layouts and source head ranges, one of them
+    empty with NULL buffers: bit-exact against the oracle's appends."""
+    need_gpu()
+    from cached_block_causal_amd import kv_append_segments
+    from cached_block_causal_amd import _lib as L
+    rng = np.random.default_rng(head_dim)
+    hr, cap = 3, 250
+    srcs = [("head", 5, 1, 17), ("token", 4, 1, 1), ("head", 3, 0, 0), ("token", 7, 4, 130)]
+    cache = poisoned_cache(hr, head_dim, cap)
+    segs, want_k, want_v, length = [], _poison_np(hr, cap, head_dim), _poison_np(hr, cap, head_dim), 0
+    for layout, src_heads, hb, n in srcs:
+        shape = (src_heads, n, head_dim) if layout == "head" else (n, src_heads, head_dim)
+        k = rng.integers(0, 0x7F00, size=shape, dtype=np.uint16)
+        v = rng.integers(0, 0x7F00, size=shape, dtype=np.uint16)
+        segs.append((dev_bits(k), dev_bits(v), layout, hb))
+        want_k, want_v, length = O.kv_append(want_k, want_v, length, k, v, hb,
+                                             O.HEAD_MAJOR if layout == "head" else O.TOKEN_MAJOR)
+    kv_append_segments(cache, segs)
+    torch.cuda.synchronize()
+    assert cache.len == length == 148
+    assert np.array_equal(host_bits(cache.k), want_k)
+    assert np.array_equal(host_bits(cache.v), want_v)
+    # too many tokens in total: refused, nothing written
+    with pytest.raises(L.WsError) as e:
+        kv_append_segments(cache, segs)
+    assert e.value.status == L.WS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert cache.len == 148
+    assert np.array_equal(host_bits(cache.k), want_k)

@@ -90,3 +90,52 @@ def test_units_against_oracle_and_one_stream(w):
         assert np.array_equal(xs1[i], xs[i])
         for s in range(w.steps):
             assert np.array_equal(outs1[i][s], outs[i][s])
+
+
+def test_rank_share_two_units_sampled_against_oracle_and_one_stream():
+    """The benched shape (v02_rank_share, 10 heads, 920 queries over ~62k keys):
+    two consecutive units with the unit-end append beside the last denoise
+    step; every step's output on two heads at sampled rows (query-tile edges
+    and random rows) against the oracle, the Euler states and the final cache
+    bit-exact, and every output bit-identical to the one-stream schedule."""
+    need_gpu()
+    w = W.V02_RANK
+    n_units = 2
+    print(f"pipeline {w.name} units {n_units}", flush=True)
+    units = _inputs(w, n_units)
+    ck, cv, length, outs, xs = _run(w, units, overlap=True)
+    sample_heads = [0, 9]
+    rng = np.random.default_rng(11)
+    rows = np.array(sorted(set([0, 1, 127, 128, 895, 896, 919] + rng.integers(0, w.n_q, 40).tolist())))
+    hk, hv = G.history_bits(w, [w.head_begin + h for h in sample_heads])
+    ids = list(G.history_unit_ids(w)[:w.history_len])
+    ek, ev, el = hk[:, :w.history_len], hv[:, :w.history_len], w.history_len
+    scale = 1 / np.sqrt(w.head_dim)
+    for i, (sk, sv, steps, x0) in enumerate(units):
+        u = w.cached_units + i
+        # the slice (this GPU's heads of the all-heads token-major source)
+        sl_k = sk[:, [w.head_begin + h for h in sample_heads]].transpose(1, 0, 2)
+        sl_v = sv[:, [w.head_begin + h for h in sample_heads]].transpose(1, 0, 2)
+        ek, ev = np.concatenate([ek, sl_k], 1), np.concatenate([ev, sl_v], 1)
+        el += sk.shape[0]
+        ids += [u] * sk.shape[0]
+        for s, (q, ks, vs, _) in enumerate(steps):
+            k, v, ku = O.streaming_keys(ek, ev, el, np.array(ids), ks[sample_heads],
+                                        vs[sample_heads], u)
+            want = O.attention(q[sample_heads][:, rows], k, v, np.full(len(rows), u), ku, scale)
+            assert_close(outs[i][s][sample_heads][:, rows], want, f"unit {i} step {s}")
+        want_x = O.fm_euler_unit(x0, [st[3] for st in steps], w.dt)
+        assert np.array_equal(xs[i], want_x), f"unit {i} Euler state"
+        ek = np.concatenate([ek, steps[-1][1][sample_heads]], 1)
+        ev = np.concatenate([ev, steps[-1][2][sample_heads]], 1)
+        el += w.n_self
+        ids += [u] * w.n_self
+    assert length == w.history_len + n_units * w.unit_tokens
+    assert np.array_equal(ck[sample_heads][:, :length], ek)
+    assert np.array_equal(cv[sample_heads][:, :length], ev)
+    ck1, cv1, length1, outs1, xs1 = _run(w, units, overlap=False)
+    assert length1 == length and np.array_equal(ck1, ck) and np.array_equal(cv1, cv)
+    for i in range(n_units):
+        assert np.array_equal(xs1[i], xs[i])
+        for s in range(w.steps):
+            assert np.array_equal(outs1[i][s], outs[i][s])
