@@ -705,8 +705,8 @@ def side_record(rec: dict) -> dict:
     out["config"] = {k: rec["config"][k] for k in ("heads", "head_dim", "n_q", "n_keys", "splits")}
     r = rec["roofline"]
     out["roofline"] = {k: r[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac",
-                                         "mfma_frac", "hbm_frac", "launch_ms_avg", "launch_ms_p50",
-                                         "step_ms_avg", "step_frac") if k in r}
+                                         "traffic", "mfma_frac", "hbm_frac", "launch_ms_avg",
+                                         "launch_ms_p50", "step_ms_avg", "step_frac") if k in r}
     if "cpu_baseline" in rec:
         c = rec["cpu_baseline"]
         out["cpu_baseline"] = {k: c[k] for k in ("value", "unit", "cores", "kind", "sample",
