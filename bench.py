@@ -714,6 +714,33 @@ def side_record(rec: dict) -> dict:
     return out
 
 
+def mfma_ceiling(reps: int = 20) -> dict:
+    """A dense bf16 product from the vendor library (torch.matmul, 8192^3) on
+    the same GPU in the same run: what its matrix cores sustain in practice,
+    beside the published peak. Context for the attention kernel's figure, not
+    part of the path."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        c = a @ b
+    t1.record()
+    torch.cuda.synchronize()
+    del a, b, c
+    ms = t0.elapsed_time(t1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"what": "torch.matmul bf16 8192 x 8192 x 8192 (vendor GEMM library), same run",
+            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -751,6 +778,12 @@ def main():
             out["workloads"][name] = side_record(rec)
             torch.cuda.empty_cache()
         out["ops"] = op_records(min(args.steps, 10))
+        out["mfma_ceiling"] = mfma_ceiling()
+        torch.cuda.empty_cache()
+        gemm = out["mfma_ceiling"]["tflops"]
+        for r in [out["roofline"]] + [v["roofline"] for v in out["workloads"].values()]:
+            if r.get("mfma_tflops") or r.get("bound") == "mfma":
+                r["frac_of_gemm"] = round((r.get("mfma_tflops") or r["achieved"]) / gemm, 4)
     print(json.dumps(out), flush=True)
 
 

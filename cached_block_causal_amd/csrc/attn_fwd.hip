@@ -185,25 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
   const bool wave_active = r0 + wave * 32 < a.n_q;
   // the unit of a row is the last non-empty unit starting at or before it
   const int kend = lane_kend<kTable>(a, qrow);
-  u32x4 qf[T::kDSteps];
-  {
-    const uint16_t* qp = a.q + ((int64_t)h * a.n_q + qrow) * D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < T::kDSteps; ++ks)
-      qf[ks] = qrow < a.n_q ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : u32x4{0, 0, 0, 0};
-    // wait for Q here, once: otherwise paths that skip the prologue leave the
-    // loads pending and every tile's first MFMA would wait on all loads
-    __builtin_amdgcn_s_waitcnt(0);
-    // fold the softmax scale (times log2 e) into Q, rounded back to bf16: the
-    // MFMAs then produce scores in log2 units and the softmax needs no
-    // multiply (one more bf16 rounding of each q element, within the
-    // tolerance of the result)
-#pragma unroll
-    for (int ks = 0; ks < T::kDSteps; ++ks)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        qf[ks][w] = pack_bf16x2(bf16_lo(qf[ks][w]) * a.scale_log2, bf16_hi(qf[ks][w]) * a.scale_log2);
-  }
+  u32x4 qf[T::kDSteps];  // loaded after the first tiles' loads are issued
 
   f32x16 o[T::kDBlocks];
 #pragma unroll
@@ -456,12 +438,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(const AttnArg
     stage_barrier();  // K(r+2), V(r+1) landed; tile r done everywhere
   };
 
+  // prologue: K and V of tile 0 and K of tile 1 into LDS, then Q, so that
+  // the first tiles and Q travel together
   if (n_t > 0) {
-    // prologue: K and V of tile 0 and K of tile 1 into LDS, S^T of tile 0
     dma_k(0, kst[0]);
     dma_v(0, vst[0]);
     dma_k(1, kst[1]);
-    stage_barrier();
+  }
+  {
+    const uint16_t* qp = a.q + ((int64_t)h * a.n_q + qrow) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+      qf[ks] = qrow < a.n_q ? *reinterpret_cast<const u32x4*>(qp + ks * 16) : u32x4{0, 0, 0, 0};
+    // wait for Q and the first tiles here, once: otherwise paths that skip
+    // the prologue leave the loads pending and every tile's first MFMA would
+    // wait on all loads
+    __builtin_amdgcn_s_waitcnt(0);
+    // fold the softmax scale (times log2 e) into Q, rounded back to bf16: the
+    // MFMAs then produce scores in log2 units and the softmax needs no
+    // multiply (one more bf16 rounding of each q element, within the
+    // tolerance of the result)
+#pragma unroll
+    for (int ks = 0; ks < T::kDSteps; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        qf[ks][w] = pack_bf16x2(bf16_lo(qf[ks][w]) * a.scale_log2, bf16_hi(qf[ks][w]) * a.scale_log2);
+  }
+  if (n_t > 0) {
+    // S^T of tile 0 once every wave's share of the first tiles has landed
+    __syncthreads();
     qk(kst[0], s_a);
     if (wave_active) prepare(0, s_a, tile_max(s_a));
     __syncthreads();  // every wave is done with K(0) before K(2) replaces it
