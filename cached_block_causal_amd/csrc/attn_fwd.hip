@@ -51,7 +51,8 @@
 //    run a narrow kernel instead: one wave per (head, split) over 32-key
 //    tiles, with its own two LDS stages and no barrier. Such a call is bound
 //    by the K/V stream; the narrow form spends 4x fewer MFMAs on empty query
-//    rows and fills the chip with more, shorter streams.
+//    rows and fills the chip with more, shorter streams, and it reads whole
+//    cache lines with non-temporal loads (each K/V byte is read once).
 #include <math.h>
 
 #include "ws_device.hpp"
@@ -75,6 +76,16 @@ struct Tile {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Chunk swizzle of the narrow kernel's LDS tiles (128-byte half rows): the
+// 16-byte chunk c of row R's half sits in slot c ^ swz(R), swz(R) = row bits
+// 1, 2, 3 reversed. Any 8 rows of one parity then spread one chunk over all
+// slots (the 16-lane passes of the K reads), and rows R and R + 2 land in
+// opposite halves of the slots (the 32-lane passes of the transposing V
+// reads): both read patterns are free of bank conflicts.
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Visible-key count of a query row from the unit table: the key end of the
@@ -518,9 +529,8 @@ template <int D, bool kTable>
 __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   using T = Tile<D>;
   constexpr int kN = kAttnNarrowN;            // keys per tile
-  constexpr int kGB = kN * 64;                // one 64-byte column group of a tile
-  constexpr int kSB = T::kGroups * kGB;       // one stage
-  constexpr int kLoads = (kN / 16) * T::kGroups;  // 1 KB loads per tile and operand
+  constexpr int kSB = kN * D * 2;             // one stage (a tile of K or V)
+  constexpr int kLoads = kSB / 1024;          // 1 KB loads per tile and operand
   __shared__ __attribute__((aligned(16))) char k_st0[kSB];
   __shared__ __attribute__((aligned(16))) char k_st1[kSB];
   __shared__ __attribute__((aligned(16))) char v_st0[kSB];
@@ -569,16 +579,38 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   float m_run = kNegInf, m_off = 0.f, l_run = 0.f;
   f32x16 neg_off = f32x16{};
 
-  // LDS layout as in the main kernel: byte (G, row, slot) = G*kGB + row*64 +
-  // slot*16 holds chunk 4G + (slot ^ ((row >> 2) & 3)); lane l of load b
-  // writes row 16b + l/4, slot l%4.
-  const uint32_t dma_off = (uint32_t)((lane >> 2) * D * 2 + (((lane & 3) ^ (lane >> 4)) * 16));
-  const int k_ofs[2] = {lrow * 64 + (((0 + half) ^ ((lrow >> 2) & 3)) * 16),
-                        lrow * 64 + (((2 + half) ^ ((lrow >> 2) & 3)) * 16)};
+  // LDS layout: byte (h, row, slot) = h*kHB + row*128 + slot*16 holds chunk
+  // slot ^ swz(row) of the row's 128-byte half h (dims 64h + 8c ..). One load
+  // moves 8 rows x 128 bytes, so each group of 8 lanes reads a whole cache
+  // line, and the loads are non-temporal: every K/V byte of the call is read
+  // once, and a stream of whole lines that does not stay in the L2 reaches
+  // the memory's pace (half lines, or lines kept in the L2, do not).
+  // Load b moves rows 8b .. 8b+7: lane l writes row 8b + l/8, slot l%8.
+  constexpr int kHB = kN * 128;   // one half of a tile
+  constexpr int kH = D / 64;      // halves per row
+  const int dma_j = lane >> 3, dma_p = lane & 7;
+  uint32_t dma_off[kN / 8];
+#pragma unroll
+  for (int b = 0; b < kN / 8; ++b)
+    dma_off[b] = (uint32_t)((8 * b + dma_j) * D * 2 + ((dma_p ^ swz(8 * b + dma_j)) * 16));
+  // K operand of MFMA ks: row lrow, dims 16ks + 8half ..: half ks/4, chunk
+  // 2(ks%4) + half; one offset per ks%4
+  int k_ofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k_ofs[j] = lrow * 128 + (((2 * j + half) ^ swz(lrow)) * 16);
+  // V^T operand of MFMA (db, ks2), read e (keys +8e): lane 16g + 4s + q reads
+  // row 16*ks2 + 8e + 4*half + s, dims db*32 + 16*(g&1) + 4q .., i.e. half
+  // db/2, chunk 4(db&1) + 2(g&1) + q/2, with swz(row) = 4(s/2) + 2half + e;
+  // one offset per (db&1, e)
   const int v_s = (lane >> 2) & 3, v_q = lane & 3, v_g1 = (lane >> 4) & 1;
   const int v_u = 2 * v_g1 + (v_q >> 1);
-  const int v_ofs[2] = {(4 * half + v_s) * 64 + ((v_u ^ (0 + half)) * 16) + 8 * (v_q & 1),
-                        (4 * half + v_s) * 64 + ((v_u ^ (2 + half)) * 16) + 8 * (v_q & 1)};
+  int v_ofs[2][2];
+#pragma unroll
+  for (int d1 = 0; d1 < 2; ++d1)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      v_ofs[d1][e] = (4 * half + v_s) * 128 + 16 * (4 * (d1 ^ (v_s >> 1)) + (v_u ^ (2 * half + e))) +
+                     8 * (v_q & 1);
 
   struct TileLoc {
     int abs_base, rows;
@@ -598,17 +630,14 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
   };
   auto dma_tile = [&](const uint16_t* rows_ptr, int rows, char* stage) {
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows_ptr, (uint32_t)rows * D * 2);
+    // (the half's byte offset is the scalar offset, inside the row, so rows
+    // past the range still read zeros; aux 2 = non-temporal)
 #pragma unroll
-    for (int b = 0; b < kN / 16; ++b) {
-      char* dst = stage + b * 1024;
-      const uint32_t off = dma_off + b * 16 * D * 2;
-      dma_group<0>(rs, dst, off);
-      dma_group<1>(rs, dst + kGB, off);
-      if constexpr (T::kGroups == 4) {
-        dma_group<2>(rs, dst + 2 * kGB, off);
-        dma_group<3>(rs, dst + 3 * kGB, off);
-      }
-    }
+    for (int b = 0; b < kN / 8; ++b)
+#pragma unroll
+      for (int h = 0; h < kH; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + h * kHB + b * 1024), 16,
+                                                 dma_off[b], h * 128, 0, 2);
   };
   auto dma = [&](int r, char* ks_stage, char* vs_stage) {
     const TileLoc L = locate(r);
@@ -621,7 +650,7 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
     f32x16 sc = neg_off;
 #pragma unroll
     for (int ks = 0; ks < T::kDSteps; ++ks)
-      sc = mfma32x32x16(lds_read16(kst, (ks >> 1) * kGB + k_ofs[ks & 1]), qf[ks], sc);
+      sc = mfma32x32x16(lds_read16(kst, (ks >> 2) * kHB + k_ofs[ks & 3]), qf[ks], sc);
     // mask the keys past the tile's rows or this row's visible range
     const TileLoc L = locate(r);
     if (__builtin_expect(L.rows < kN || L.abs_base + kN > kmin, 0)) {
@@ -661,9 +690,9 @@ __global__ __launch_bounds__(64) void attn_narrow_kernel(const AttnArgs a) {
     for (int db = 0; db < T::kDBlocks; ++db)
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const char* b = vst + db * kGB + 16 * ks2 * 64;
-        const u32x2 lo = lds_read_tr(b, v_ofs[0]);
-        const u32x2 hi = lds_read_tr(b + 8 * 64, v_ofs[1]);
+        const char* b = vst + (db >> 1) * kHB + 16 * ks2 * 128;
+        const u32x2 lo = lds_read_tr(b, v_ofs[db & 1][0]);
+        const u32x2 hi = lds_read_tr(b + 8 * 128, v_ofs[db & 1][1]);
         o[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks2], o[db]);
       }
   };
