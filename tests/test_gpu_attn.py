@@ -1,9 +1,9 @@
 """ws_block_causal_attn on the GPU against the fp64 oracle, on every workload.
 
 Small workloads are compared on every output element; the full-size video
-workloads on every output of every head at denoise step 0, and on sampled
-heads and rows at the later steps; the audio workload on every output of
-eight heads (the oracle computes each head independently).
+workloads, the audio workload and the joint call on every output of every
+head at one denoise step, and on sampled heads and rows at the later steps
+(the oracle computes each head independently).
 Unused cache capacity is poisoned with NaN, so any read past the valid rows
 would show up as a non-finite output.
 """
@@ -104,13 +104,36 @@ def test_v02_whole_performer_later_steps_sampled_rows():
 @pytest.mark.timeout(600)
 def test_audio_long_history_sampled_heads():
     need_gpu()
-    _streaming_case(W.AUDIO_LONG, [0, 3], heads_sampled=[0, 5, 10, 13, 20, 27, 33, 39])
+    _streaming_case(W.AUDIO_LONG, [3], heads_sampled=[0, 5, 10, 13, 20, 27, 33, 39])
 
 
 @pytest.mark.timeout(600)
-def test_joint_audio_video_call_sampled_heads():
+def test_audio_long_history_every_head():
+    """All 40 heads x 4 queries x 244,772 keys of denoise step 0; the oracle
+    takes the heads eight at a time to bound host memory."""
+    need_gpu()
+    from cached_block_causal_amd import AttnCall
+    w = W.AUDIO_LONG
+    print(f"attn {w.name} step 0 every head", flush=True)
+    cache = poisoned_cache(w.heads, w.head_dim, w.capacity)
+    fill_history(cache, w)
+    q, ks, vs, _ = G.step_tensors(w, 0)
+    out = host_bits(AttnCall(cache, dev_bits(q), dev_bits(ks), dev_bits(vs)).run())
+    ids = G.history_unit_ids(w)
+    results = []
+    for h0 in range(0, w.heads, 8):
+        sel = list(range(h0, min(w.heads, h0 + 8)))
+        hk, hv = G.history_bits(w, [w.head_begin + h for h in sel])
+        k, v, ku = O.streaming_keys(hk, hv, w.cache_len, ids, ks[sel], vs[sel], w.current_unit)
+        want = O.attention(q[sel], k, v, np.full(w.n_q, w.current_unit), ku, 1 / np.sqrt(w.head_dim))
+        results.append(assert_close(out[sel], want, f"{w.name} heads {sel[0]}-{sel[-1]}"))
+    print(results, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_joint_audio_video_call_every_head():
     """The unit's audio and video queries in one call (audio rows first): on
-    sampled heads every row equals the oracle, where the audio rows see the
+    every head every row equals the oracle, where the audio rows see the
     cache and the unit's audio tokens and the video rows also the unit's
     video tokens; the audio rows also agree with a call for audio alone."""
     need_gpu()
@@ -126,18 +149,19 @@ def test_joint_audio_video_call_sampled_heads():
     a = w.audio_tokens
     alone = host_bits(AttnCall(cache, dev_bits(q[:, :a].copy()), dev_bits(ks[:, :a].copy()),
                                dev_bits(vs[:, :a].copy())).run())
-    sel = [0, 9]
-    hk, hv = G.history_bits(w, [w.head_begin + h for h in sel])
     ids = G.history_unit_ids(w)
     u = w.current_unit
-    k = np.concatenate([O.bf16_to_f64(hk), O.bf16_to_f64(ks[sel])], axis=1)
-    v = np.concatenate([O.bf16_to_f64(hv), O.bf16_to_f64(vs[sel])], axis=1)
     ku = np.concatenate([ids, np.full(a, u), np.full(w.video_tokens, u + 1)])
     qu = np.concatenate([np.full(a, u), np.full(w.video_tokens, u + 1)])
-    want = O.attention(q[sel], k, v, qu, ku, 1 / np.sqrt(w.head_dim))
-    print(assert_close(out[sel], want, "joint call"), flush=True)
-    assert_close(alone[sel], want[:, :a], "audio alone")
-    assert_close(out[sel][:, :a], want[:, :a], "joint audio rows")
+    for h0 in range(0, w.heads, 2):              # every head, two at a time
+        sel = [h0, h0 + 1]
+        hk, hv = G.history_bits(w, [w.head_begin + h for h in sel])
+        k = np.concatenate([O.bf16_to_f64(hk), O.bf16_to_f64(ks[sel])], axis=1)
+        v = np.concatenate([O.bf16_to_f64(hv), O.bf16_to_f64(vs[sel])], axis=1)
+        want = O.attention(q[sel], k, v, qu, ku, 1 / np.sqrt(w.head_dim))
+        print(assert_close(out[sel], want, f"joint call heads {sel}"), flush=True)
+        assert_close(alone[sel], want[:, :a], f"audio alone heads {sel}")
+        assert_close(out[sel][:, :a], want[:, :a], f"joint audio rows heads {sel}")
 
 
 def _multi_unit_tiny():
